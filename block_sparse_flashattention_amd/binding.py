@@ -1,0 +1,267 @@
+"""Thin Python binding over libbsfa.so (argument marshalling only).
+
+Names follow the C ABI in include/bsfa.h: ``build_block_lists``, ``fwd``,
+``skip_stats``. PyTorch supplies device memory and the current stream; every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the library is
+missing or a call fails, a ``BsfaError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+BSFA_CLS_PARTIAL = 1
+BSFA_CLS_FORCED = 2
+OUT_BF16, OUT_F32 = 0, 1
+
+
+class BsfaError(RuntimeError):
+    """A libbsfa call returned a non-zero status (message from bsfa_last_error)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libbsfa status {status}: {message}")
+        self.status = status
+
+
+class _CMask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("n_global", ctypes.c_int32), ("force_keep_diag", ctypes.c_int32),
+                ("force_keep_global", ctypes.c_int32)]
+
+
+class _CStrides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class _CLists(ctypes.Structure):
+    _fields_ = [("n_qtiles", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p),
+                ("cls", ctypes.c_void_p)]
+
+
+EXPORTED = ("bsfa_build_block_lists", "bsfa_fwd", "bsfa_skip_stats", "bsfa_last_error",
+            "bsfa_abi_version")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libbsfa.so")
+
+
+def load_library():
+    """Load libbsfa.so (once). Raises BsfaError if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise BsfaError(-4, f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.bsfa_build_block_lists.argtypes = [
+        P(_CMask), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, P(ctypes.c_int64)]
+    lib.bsfa_build_block_lists.restype = ctypes.c_int
+    lib.bsfa_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        P(_CStrides), P(_CStrides), P(_CStrides), P(_CStrides), P(_CMask), P(_CLists),
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsfa_fwd.restype = ctypes.c_int
+    lib.bsfa_skip_stats.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsfa_skip_stats.restype = ctypes.c_int
+    lib.bsfa_last_error.argtypes = []
+    lib.bsfa_last_error.restype = ctypes.c_char_p
+    lib.bsfa_abi_version.argtypes = []
+    lib.bsfa_abi_version.restype = ctypes.c_int32
+    _LIB = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise BsfaError(status, lib.bsfa_last_error().decode(errors="replace"))
+
+
+@dataclass(frozen=True)
+class MaskSpec:
+    """Static pattern: causal AND (window OR global tokens); see include/bsfa.h."""
+
+    causal: bool = True
+    window: int = 0
+    n_global: int = 0
+    force_keep_diag: bool = True
+    force_keep_global: bool = True
+
+    def _c(self) -> _CMask:
+        return _CMask(int(self.causal), int(self.window), int(self.n_global),
+                      int(self.force_keep_diag), int(self.force_keep_global))
+
+
+def build_block_lists(mask: MaskSpec, n: int, block_q: int = 64, block_k: int = 64):
+    """Host CSR of allowed tiles: (row_ptr int32 [nqt+1], col int32 [nnz], cls uint8 [nnz])."""
+    lib = load_library()
+    cm = mask._c()
+    nnz = ctypes.c_int64(0)
+    nqt = (n + block_q - 1) // block_q
+    row_ptr = np.zeros(nqt + 1, dtype=np.int32)
+    _check(lib, lib.bsfa_build_block_lists(ctypes.byref(cm), n, block_q, block_k,
+                                           row_ptr.ctypes.data, None, None, 0,
+                                           ctypes.byref(nnz)))
+    col = np.zeros(max(nnz.value, 1), dtype=np.int32)
+    cls = np.zeros(max(nnz.value, 1), dtype=np.uint8)
+    _check(lib, lib.bsfa_build_block_lists(ctypes.byref(cm), n, block_q, block_k,
+                                           row_ptr.ctypes.data, col.ctypes.data,
+                                           cls.ctypes.data, col.size, ctypes.byref(nnz)))
+    return row_ptr, col[: nnz.value], cls[: nnz.value]
+
+
+class BlockLists:
+    """Device copy of the 64x64 block lists for one (mask, N)."""
+
+    _cache: dict = {}
+
+    def __init__(self, mask: MaskSpec, n: int, device):
+        import torch
+
+        row_ptr, col, cls = build_block_lists(mask, n, 64, 64)
+        self.mask, self.n = mask, n
+        self.n_qtiles = row_ptr.size - 1
+        self.nnz = int(col.size)
+        self.row_ptr_host, self.col_host, self.cls_host = row_ptr, col, cls
+        self.row_ptr = torch.from_numpy(row_ptr).to(device)
+        self.col = torch.from_numpy(col if col.size else np.zeros(1, np.int32)).to(device)
+        self.cls = torch.from_numpy(cls if cls.size else np.zeros(1, np.uint8)).to(device)
+
+    @classmethod
+    def get(cls, mask: MaskSpec, n: int, device) -> "BlockLists":
+        key = (mask, n, str(device))
+        if key not in cls._cache:
+            cls._cache[key] = cls(mask, n, device)
+        return cls._cache[key]
+
+    def _c(self) -> _CLists:
+        return _CLists(self.n_qtiles, 64, 64, self.nnz, self.row_ptr.data_ptr(),
+                       self.col.data_ptr(), self.cls.data_ptr())
+
+
+@dataclass
+class FwdResult:
+    out: object
+    lse: object
+    stats: object = None  # uint64 view as int64 tensor [B, Hq, 2] {kept, skipped}
+    tile_max: object = None  # fp32 [B, Hq, nnz]
+    keep: object = None  # uint8 [B, Hq, nnz]
+    lists: BlockLists = None
+
+
+def _strides(t) -> _CStrides:
+    s = t.stride()
+    if s[3] != 1:
+        raise BsfaError(-2, "the head dimension must be contiguous")
+    return _CStrides(s[0], s[1], s[2])
+
+
+def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0.0,
+        out_dtype=None, out=None, want_lse: bool = True, stats: bool = False,
+        export_tiles: bool = False, lists: BlockLists | None = None, stream=None) -> FwdResult:
+    """Block-sparse attention forward on the GPU (asynchronous on the current stream).
+
+    q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d] (CUDA/HIP tensors, last dim
+    contiguous). tau: None (dense path) or fp32 tensor [Hq] on the device (or anything
+    torch.as_tensor accepts). Returns out [B, Hq, N, d] (bf16 or fp32), lse fp32
+    [B, Hq, N], optional per-(b, h) {kept, skipped} counts and per-tile export.
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise BsfaError(-1, "q, k, v must be 4-D [B, H, N, d]")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise BsfaError(-2, "q, k, v must be bfloat16")
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if tuple(k.shape) != (bsz, hkv, n, d) or tuple(v.shape) != (bsz, hkv, n, d):
+        raise BsfaError(-1, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    dev = q.device
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if out is None:
+        out = torch.empty((bsz, hq, n, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((bsz, hq, n), dtype=torch.float32, device=dev) if want_lse else None
+    if lists is None:
+        lists = BlockLists.get(mask, n, dev)
+    tau_t = None
+    if tau is not None:
+        tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
+        if tau_t.numel() == 1 and hq > 1:
+            tau_t = tau_t.expand(hq).contiguous()
+        if tau_t.numel() != hq:
+            raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
+        tau_t = tau_t.contiguous()
+    st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
+    tm = kp = None
+    if export_tiles:
+        tm = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.float32, device=dev)
+        kp = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    cm = mask._c()
+    cl = lists._c()
+    sq, sk, sv, so = _strides(q), _strides(k), _strides(v), _strides(out)
+    status = lib.bsfa_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, bsz, hq, hkv, n, d,
+        ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
+        ctypes.byref(cm), ctypes.byref(cl),
+        tau_t.data_ptr() if tau_t is not None else None, float(softmax_scale),
+        OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
+        st.data_ptr() if st is not None else None,
+        tm.data_ptr() if tm is not None else None,
+        kp.data_ptr() if kp is not None else None, stream)
+    _check(lib, status)
+    if tm is not None and lists.nnz == 0:
+        tm, kp = tm[..., :0], kp[..., :0]
+    return FwdResult(out, lse, st, tm, kp, lists)
+
+
+def skip_stats(stats_tensor, stream=None):
+    """{kept, skipped} tile counts per (b, h) as two uint64 numpy arrays [B, Hq]."""
+    import torch
+
+    lib = load_library()
+    bsz, hq, _ = stats_tensor.shape
+    kept = np.zeros((bsz, hq), dtype=np.uint64)
+    skipped = np.zeros((bsz, hq), dtype=np.uint64)
+    if stream is None:
+        stream = torch.cuda.current_stream(stats_tensor.device).cuda_stream
+    _check(lib, lib.bsfa_skip_stats(stats_tensor.data_ptr(), bsz, hq, kept.ctypes.data,
+                                    skipped.ctypes.data, stream))
+    return kept, skipped
+
+
+def calibrate_tau(q, k, mask: MaskSpec, quantile: float, softmax_scale: float = 0.0):
+    """Per-head threshold: the ``quantile`` of the eligible (allowed, not forced) block
+    maxima of each query head, measured on calibration inputs q, k with the gated kernel
+    at tau = -inf (nothing skipped) and its per-tile export. Returns fp32 numpy [Hq]."""
+    import torch
+
+    hq = q.shape[1]
+    res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), -math.inf, device=q.device),
+              softmax_scale=softmax_scale, want_lse=False, export_tiles=True)
+    tmax = res.tile_max.float().cpu().numpy()  # [B, Hq, nnz]
+    eligible = (res.lists.cls_host & BSFA_CLS_FORCED) == 0
+    taus = np.empty(hq, dtype=np.float32)
+    for h in range(hq):
+        vals = tmax[:, h, :][:, eligible].reshape(-1)
+        taus[h] = np.quantile(vals, quantile) if vals.size else -np.inf
+    return taus

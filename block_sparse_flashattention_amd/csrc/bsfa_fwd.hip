@@ -1,0 +1,409 @@
+// Block-sparse FlashAttention forward (prefill) for gfx950 (MI355X).
+//
+// Method: exact tiled attention with a running softmax ("sparse attention mechanism"
+// glossary page, section "FlashAttention") plus the Block Sparse FlashAttention gate
+// (AI Radio episode "Block Sparse Flash Attention", "The paper's summary" and "The
+// paper's improvements"): for every (64-row query tile, 64-key block) the exact scores
+// are computed first, their maximum is compared with a per-head threshold tau_h, and a
+// block below it is dropped from the softmax and its V block is never loaded.
+//
+// Work decomposition
+//   One workgroup = one 64-row query tile of HPACK query heads that share a KV head
+//   (grouped-query attention), so each staged K/V block feeds HPACK heads. Two waves
+//   per head, 32 query rows per wave: 128 * HPACK threads.
+//
+// Register layout (v_mfma_f32_32x32x16_bf16; lane l, half h = l / 32, l32 = l % 32)
+//   Scores are computed transposed, S^T = K Q^T (keys x queries), so a lane owns ONE
+//   query row (l32) and 32 of its 64 keys: key = 32*mt + 8*(i/4) + 4*h + i%4 for
+//   accumulator element i of key tile mt. The running max m and sum l are therefore
+//   per-lane scalars; a row reduction is a local loop plus one exchange with lane l^32.
+//   P^T then feeds the P.V MFMA (O^T = V^T P^T) as its B operand straight from the
+//   accumulator registers: for 16-key step ks the lane's 8 values are accumulator
+//   elements 8*(ks%2) .. +7 of tile ks/2. V^T rows come from a row-major V tile in LDS
+//   via ds_read_tr16_b64 (two 4-key reads per operand).
+//
+// The gate's tile maximum: local max over 32 values, DPP all-reduce inside each
+// 16-lane row, readlane across rows, then one LDS slot per wave and a barrier, so the
+// keep/skip branch is uniform across the workgroup.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/bsfa.h"
+#include "bsfa_internal.h"
+
+namespace bsfa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BLK = 64;
+
+__device__ __forceinline__ float dpp_max(float x, int ctrl_sel) {
+  // all lanes valid for the row/quad permutations used here
+  int y;
+  switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad [1,0,3,2]
+    case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad [2,3,0,1]
+    case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false); break;  // row_ror:4
+    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false); break; // row_ror:8
+  }
+  return fmaxf(x, __int_as_float(y));
+}
+
+// Maximum over the 64 lanes of a wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_max(float x) {
+  x = dpp_max(x, 0);
+  x = dpp_max(x, 1);
+  x = dpp_max(x, 2);
+  x = dpp_max(x, 3);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// {x[l], x[l ^ 32]} in some order, for every lane l.
+__device__ __forceinline__ void pair32(float x, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bool allowed(int i, int j, int n, int causal, int window, int ng) {
+  if (i >= n || j >= n) return false;
+  if (causal && j > i) return false;
+  if (window > 0) {
+    const int dist = i > j ? i - j : j - i;
+    if (!(dist < window || j < ng || i < ng)) return false;
+  }
+  return true;
+}
+
+template <int D, int NT>
+struct TileIO {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int CPT = BLK * CPR / NT;     // chunks per thread
+  static_assert(BLK * CPR % NT == 0, "tile chunks must divide evenly");
+
+  // Rows [c*64, c*64+64) of a [N, D] bf16 matrix (row stride sn) into registers;
+  // rows at or past n read as zeros.
+  __device__ __forceinline__ static void load(u32x4_t (&r)[CPT], const uint16_t* base,
+                                              int64_t sn, int c, int n, int tid) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * NT;
+      const int row = ch / CPR, cc = ch % CPR;
+      const int key = c * BLK + row;
+      if (c >= 0 && key < n)
+        r[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)key * sn + cc * 8);
+      else
+        r[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  template <int ROWSTRIDE>
+  __device__ __forceinline__ static void store(uint16_t* s, const u32x4_t (&r)[CPT], int tid) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * NT;
+      const int row = ch / CPR, cc = ch % CPR;
+      *reinterpret_cast<u32x4_t*>(s + row * ROWSTRIDE + cc * 8) = r[i];
+    }
+  }
+};
+
+template <int D, int HPACK, bool SKIP, bool OUT_F32>
+__global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) {
+  constexpr int NW = 2 * HPACK;  // waves per workgroup
+  constexpr int NT = 64 * NW;    // threads per workgroup
+  constexpr int KS = D / 16;     // 16-wide steps along d for S^T = K Q^T
+  constexpr int DT = D / 32;     // 32-row tiles of O^T along d
+  constexpr int KROW = D + 8;    // K tile row stride in LDS (elements): +16 B pad
+  constexpr int VROW = D + 16;   // V tile row stride in LDS (elements): +32 B pad
+  using IO = TileIO<D, NT>;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BLK * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BLK * VROW];
+  __shared__ float sRed[NW];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // ---- which (batch, head pack, query tile) this workgroup owns.
+  // Workgroups are dealt round-robin to the 8 XCDs; when the number of (batch, pack)
+  // pairs is a multiple of 8, consecutive packs (same KV head) land on the same XCD,
+  // so its L2 serves one KV head's K/V. Query tiles run longest-row first.
+  const int packs = a.Hq / HPACK;
+  const int P = a.B * packs;
+  const int wg = blockIdx.x;
+  int p, trank;
+  if (P % 8 == 0) {
+    const int per = P / 8;
+    p = (wg % 8) * per + (wg / 8) % per;
+    trank = wg / P;
+  } else {
+    p = wg % P;
+    trank = wg / P;
+  }
+  const int b = p / packs, hp = p % packs;
+  const int t = a.nqt - 1 - trank;
+  const int hq = hp * HPACK + (wave >> 1);
+  const int g = hq / a.group;
+  const int qi = t * BLK + (wave & 1) * 32 + l32;  // this lane's query row
+
+  // ---- Q^T fragments (B operand of S^T = K Q^T): d = 16*ks + 8*half + [0, 8)
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = a.q + (int64_t)b * a.sqb + (int64_t)hq * a.sqh + (int64_t)qi * a.sqn;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (qi < a.N)
+        qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16 + half * 8);
+      else
+        qf[ks] = bf16x8_t{};
+    }
+  }
+
+  float tau_pack[HPACK];
+#pragma unroll
+  for (int j = 0; j < HPACK; ++j) tau_pack[j] = SKIP ? a.tau[hp * HPACK + j] : 0.0f;
+
+  int e0 = a.row_ptr[t], e1 = a.row_ptr[t + 1];
+  e0 = e0 < 0 ? 0 : (e0 > a.nnz ? (int)a.nnz : e0);
+  e1 = e1 < e0 ? e0 : (e1 > a.nnz ? (int)a.nnz : e1);
+
+  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)g * a.skh;
+  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)g * a.svh;
+
+  float m_run = -INFINITY;  // running max of raw q.k over kept keys of this row
+  float l_run = 0.0f;       // this lane's share of the running sum
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
+  unsigned n_kept = 0, n_skip = 0;
+
+  u32x4_t kr[IO::CPT], vr[IO::CPT];
+  if (e0 < e1) {
+    IO::load(kr, kbase, a.skn, a.col[e0], a.N, tid);
+    IO::template store<KROW>(sK[0], kr, tid);
+  }
+
+  for (int e = e0; e < e1; ++e) {
+    const int buf = (e - e0) & 1;
+    const int c = a.col[e];
+    const int cls = a.cls[e];
+    const bool has_next = e + 1 < e1;
+    if (has_next) IO::load(kr, kbase, a.skn, a.col[e + 1], a.N, tid);
+    __syncthreads();  // K(e) staged; every wave is done with iteration e-1
+
+    // ---- S^T = K(e) Q^T for this wave's 32 queries: two 32x32 key tiles
+    f32x16_t s[2];
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            &sK[buf][(mt * 32 + l32) * KROW + ks * 16 + half * 8]);
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
+      }
+    }
+    if (cls & BSFA_CLS_PARTIAL) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = c * BLK + mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (!allowed(qi, j, a.N, a.causal, a.window, a.n_global)) s[mt][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
+
+    bool keep_h = true, any_keep = true;
+    float tmax_h = 0.0f;
+    if constexpr (SKIP) {
+      const float wm = wave_max(mx);
+      if (lane == 0) sRed[wave] = wm;
+      if (has_next) IO::template store<KROW>(sK[buf ^ 1], kr, tid);
+      __syncthreads();  // block maxima of every wave visible
+      const bool forced = (cls & BSFA_CLS_FORCED) != 0;
+      any_keep = false;
+#pragma unroll
+      for (int j = 0; j < HPACK; ++j) {
+        const float tm = fmaxf(sRed[2 * j], sRed[2 * j + 1]) * a.scale;
+        const bool kj = forced || (tm >= tau_pack[j]);
+        if (j == (wave >> 1)) {
+          keep_h = kj;
+          tmax_h = tm;
+        }
+        any_keep = any_keep || kj;
+      }
+    } else {
+      if (has_next) IO::template store<KROW>(sK[buf ^ 1], kr, tid);
+    }
+
+    if (any_keep) {
+      IO::load(vr, vbase, a.svn, c, a.N, tid);
+      IO::template store<VROW>(sV, vr, tid);
+      __syncthreads();  // V(e) staged
+      if (keep_h) {
+        // ---- online softmax for this lane's query row (raw-score units)
+        float x0, x1;
+        pair32(mx, x0, x1);
+        const float m_new = fmaxf(m_run, fmaxf(x0, x1));
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.scale_log2);
+        const float mb = m_use * a.scale_log2;
+        float rs = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][i], a.scale_log2, -mb));
+            s[mt][i] = pv;
+            rs += pv;
+          }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+
+        // ---- O^T += V^T P^T
+        const int vrow = 4 * half + ((lane & 15) >> 2);
+        const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8_t pb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[ks >> 1][8 * (ks & 1) + j];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint16_t* p0 = &sV[(16 * ks + vrow) * VROW + 32 * dt + vcol];
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(p0));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(p0 + 8 * VROW));
+            // Whole-vector concatenation and bit cast: an element-by-element copy from
+            // the two i16x4 results into a bf16x8 is lowered with a wrong v_perm_b32
+            // (it duplicated element 0) by this compiler.
+            const i16x8_t cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, cat);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (keep_h) ++n_kept; else ++n_skip;
+    if (SKIP && a.tile_max && (wave & 1) == 0 && lane == 0) {
+      const int64_t idx = ((int64_t)b * a.Hq + hq) * a.nnz + e;
+      a.tile_max[idx] = tmax_h;
+      a.keep[idx] = keep_h ? 1 : 0;
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = scale * m + ln l; one store per element
+  float l0, l1;
+  pair32(l_run, l0, l1);
+  const float l_tot = l0 + l1;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qi < a.N) {
+    if (a.lse && half == 0) {
+      a.lse[((int64_t)b * a.Hq + hq) * a.N + qi] =
+          l_tot > 0.0f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+    }
+    const int64_t obase = (int64_t)b * a.sob + (int64_t)hq * a.soh + (int64_t)qi * a.son;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * dt + 8 * r + 4 * half;
+        if constexpr (OUT_F32) {
+          float* op = reinterpret_cast<float*>(a.out) + obase + d0;
+          *reinterpret_cast<float4*>(op) =
+              make_float4(o[dt][4 * r] * inv, o[dt][4 * r + 1] * inv, o[dt][4 * r + 2] * inv,
+                          o[dt][4 * r + 3] * inv);
+        } else {
+          uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + obase + d0;
+          u32x2_t w;
+          const __bf16 v0 = (__bf16)(o[dt][4 * r] * inv), v1 = (__bf16)(o[dt][4 * r + 1] * inv);
+          const __bf16 v2 = (__bf16)(o[dt][4 * r + 2] * inv), v3 = (__bf16)(o[dt][4 * r + 3] * inv);
+          w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+          w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+          *reinterpret_cast<u32x2_t*>(op) = w;
+        }
+      }
+  }
+  if (a.stats && (wave & 1) == 0 && lane == 0) {
+    unsigned long long* st = a.stats + ((int64_t)b * a.Hq + hq) * 2;
+    atomicAdd(st, (unsigned long long)n_kept);
+    atomicAdd(st + 1, (unsigned long long)n_skip);
+  }
+}
+
+template <int D, int HPACK, bool SKIP, bool OUT_F32>
+hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)a.B * (a.Hq / HPACK) * a.nqt);
+  hipLaunchKernelGGL((bsfa_fwd_kernel<D, HPACK, SKIP, OUT_F32>), dim3(grid), dim3(128 * HPACK),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int HPACK>
+hipError_t launch_hpack(const FwdArgs& a, bool out_f32, hipStream_t s) {
+  const bool skip = a.tau != nullptr;
+  if (skip)
+    return out_f32 ? launch_variant<D, HPACK, true, true>(a, s)
+                   : launch_variant<D, HPACK, true, false>(a, s);
+  return out_f32 ? launch_variant<D, HPACK, false, true>(a, s)
+                 : launch_variant<D, HPACK, false, false>(a, s);
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, int hpack, bool out_f32, hipStream_t s) {
+  switch (hpack) {
+    case 4: return launch_hpack<D, 4>(a, out_f32, s);
+    case 2: return launch_hpack<D, 2>(a, out_f32, s);
+    default: return launch_hpack<D, 1>(a, out_f32, s);
+  }
+}
+
+}  // namespace
+
+int launch_fwd(const FwdArgs& a, int d, int hpack, bool out_f32, void* stream, const char** err) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = d == 64 ? launch_d<64>(a, hpack, out_f32, s) : launch_d<128>(a, hpack, out_f32, s);
+  if (e != hipSuccess) {
+    *err = hipGetErrorString(e);
+    return BSFA_ERR_HIP;
+  }
+  return BSFA_OK;
+}
+
+int copy_to_host_sync(void* dst, const void* src, size_t bytes, void* stream, const char** err) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    *err = hipGetErrorString(e);
+    return BSFA_ERR_HIP;
+  }
+  return BSFA_OK;
+}
+
+}  // namespace bsfa

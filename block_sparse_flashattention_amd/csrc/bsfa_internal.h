@@ -1,0 +1,46 @@
+// Internal interface between the host library (bsfa_host.cpp) and the HIP kernels
+// (bsfa_fwd.hip). Not part of the public C ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsfa {
+
+// Everything one forward launch needs, passed by value as the kernel argument.
+struct FwdArgs {
+  const uint16_t* q;  // bf16 bits [B, Hq, N, d]
+  const uint16_t* k;  // bf16 bits [B, Hkv, N, d]
+  const uint16_t* v;  // bf16 bits [B, Hkv, N, d]
+  void* out;          // bf16 or fp32 [B, Hq, N, d]
+  float* lse;         // fp32 [B, Hq, N] or null
+  int64_t sqb, sqh, sqn;
+  int64_t skb, skh, skn;
+  int64_t svb, svh, svn;
+  int64_t sob, soh, son;
+  int32_t B, Hq, Hkv, N;
+  int32_t nqt;    // ceil(N / 64)
+  int32_t group;  // Hq / Hkv
+  int32_t causal, window, n_global;
+  const int32_t* row_ptr;  // CSR of allowed tiles, device
+  const int32_t* col;
+  const uint8_t* cls;
+  int64_t nnz;
+  const float* tau;        // [Hq] or null (dense path)
+  float scale;             // softmax scale applied to q.k
+  float scale_log2;        // scale * log2(e)
+  unsigned long long* stats;  // [B*Hq*2] or null
+  float* tile_max;            // [B*Hq*nnz] or null
+  uint8_t* keep;              // [B*Hq*nnz] or null
+};
+
+// Launches the forward kernel variant for head dim d, head pack hpack (query heads of
+// one KV group sharing a workgroup), gated (tau != null) or dense, bf16 or fp32 output.
+// Returns 0 or a negative bsfa_status; *err receives a static message on failure.
+int launch_fwd(const FwdArgs& a, int d, int hpack, bool out_f32, void* stream,
+               const char** err);
+
+// Device-to-host copy on `stream`, then synchronise the stream. 0 or BSFA_ERR_HIP.
+int copy_to_host_sync(void* dst, const void* src, size_t bytes, void* stream,
+                      const char** err);
+
+}  // namespace bsfa

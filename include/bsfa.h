@@ -1,0 +1,161 @@
+/*
+ * bsfa.h -- C ABI of the block-sparse FlashAttention prefill library (libbsfa.so).
+ *
+ * What the library computes. For every batch b, query head h (key/value head
+ * g = h / (Hq / Hkv), grouped-query sharing as in the "Multi-Query and Grouped-Query
+ * Attention" section of the "sparse attention mechanism" glossary page) and query row i:
+ *
+ *   s_ij   = scale * q_i . k_j                      ("Standard Attention Bottleneck")
+ *   A(i,j) = static mask: causal AND (window OR global tokens)        (see mask spec)
+ *   M_tc   = max of s_ij over the allowed elements of query tile t x key block c
+ *            (64 x 64 elements)
+ *   keep   = forced(t,c) OR M_tc >= tau_h            (Block Sparse Flash Attention,
+ *            "The paper's summary" / "The paper's improvements": a calibrated
+ *            per-head threshold on each block's maximum; blocks below it are skipped)
+ *   K_i    = { j : A(i,j) and keep(i/64, j/64) }     (the index set G of the page
+ *            "Sparse attention weights assumption", "Sparse Attention Output Formula")
+ *   LSE_i  = log sum_{j in K_i} exp(s_ij);   O_i = sum_{j in K_i} exp(s_ij - LSE_i) v_j
+ *
+ * Skipped blocks leave both the numerator and the denominator of the softmax (the kept
+ * weights are renormalised), and their V block is never read. A row with an empty K_i
+ * gets O_i = 0 and LSE_i = -inf. The tiles are processed FlashAttention-style with a
+ * running max and sum ("sparse attention mechanism" glossary, "FlashAttention"), so no
+ * N x N matrix exists anywhere.
+ *
+ * Conventions for every entry point:
+ * - All functions are thread-safe, allocate no device memory and keep no per-call state.
+ * - Buffers are owned by the caller. "device" means HIP device memory on the current
+ *   device; "host" means ordinary host memory.
+ * - Return value: BSFA_OK (0) or a negative bsfa_status. On failure
+ *   bsfa_last_error() returns a thread-local message. Argument checks happen before any
+ *   work is queued, so a failed call has no side effects.
+ * - Kernel faults are asynchronous: they surface at the caller's next synchronisation.
+ */
+#ifndef BSFA_H
+#define BSFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSFA_OK = 0,
+  BSFA_ERR_INVALID_ARG = -1,      /* null pointer, negative size, inconsistent shapes   */
+  BSFA_ERR_UNSUPPORTED = -2,      /* valid but not implemented (head dim, alignment)    */
+  BSFA_ERR_BUFFER_TOO_SMALL = -3, /* block-list capacity below the required entry count */
+  BSFA_ERR_HIP = -4               /* a HIP runtime call failed; message has the reason  */
+} bsfa_status;
+
+typedef enum { BSFA_OUT_BF16 = 0, BSFA_OUT_F32 = 1 } bsfa_out_dtype;
+
+/* Block classes (bit flags in bsfa_block_lists.cls). */
+#define BSFA_CLS_PARTIAL 1u /* some element of the 64x64 tile is masked: test per element */
+#define BSFA_CLS_FORCED 2u  /* the gate never skips this tile                              */
+
+/*
+ * Static sparsity primitives, OR-composed as in "SAS: Sparse Attention Synthesizer",
+ * Step 5 (Logic Operators). Element (i, j), 0-based, with 0 <= i, j < N is allowed iff
+ *   (!causal || j <= i) && (window == 0 || |i - j| < window || j < n_global || i < n_global).
+ * With causal set, the window is the glossary page's [max(0, i - W + 1), i] ("Mistral/
+ * Mixtral Sliding Window Attention"); global tokens follow "Global Tokens in Attention"
+ * (the first tokens are visible to all, and see all). Forcing: the tile holding a
+ * diagonal element (i, i) is never skipped when force_keep_diag != 0, and tiles holding
+ * a key j < n_global are never skipped when force_keep_global != 0.
+ */
+typedef struct {
+  int32_t causal;
+  int32_t window;
+  int32_t n_global;
+  int32_t force_keep_diag;
+  int32_t force_keep_global;
+} bsfa_mask_spec;
+
+/* Element strides of a [B, H, N, d] tensor; the d dimension must be contiguous. */
+typedef struct {
+  int64_t b, h, n;
+} bsfa_strides;
+
+/*
+ * Static block lists in CSR form, shared by every batch entry and head: query tile t
+ * owns entries [row_ptr[t], row_ptr[t+1]), each a key block index col[e] (ascending)
+ * and a class cls[e] (BSFA_CLS_* flags). Tiles with no allowed element are absent.
+ * For bsfa_fwd the three arrays are in device memory and must come from
+ * bsfa_build_block_lists for the same mask spec, N and 64x64 blocks.
+ */
+typedef struct {
+  int32_t n_qtiles; /* ceil(N / block_q)                    */
+  int32_t block_q;  /* must be 64 for bsfa_fwd              */
+  int32_t block_k;  /* must be 64 for bsfa_fwd              */
+  int64_t nnz;      /* entries in col / cls                 */
+  const int32_t* row_ptr; /* [n_qtiles + 1] */
+  const int32_t* col;     /* [nnz]          */
+  const uint8_t* cls;     /* [nnz]          */
+} bsfa_block_lists;
+
+/*
+ * Build the static block lists on the host (pure CPU; no HIP call).
+ *   mask            : static pattern (host).
+ *   N               : sequence length, N >= 0 (N need not be a multiple of the block).
+ *   block_q, block_k: tile sizes, >= 1.
+ *   row_ptr         : host [ceil(N/block_q) + 1], always written (may be NULL to only
+ *                     size the lists).
+ *   col, cls        : host [capacity]; if col == NULL only *nnz_out is computed
+ *                     (two-call sizing).
+ *   nnz_out         : host, receives the number of entries. Required.
+ * Returns BSFA_ERR_BUFFER_TOO_SMALL (with *nnz_out set) when capacity < nnz.
+ * A tile is PARTIAL when any of its block_q x block_k element slots (including slots
+ * past N in a ragged last tile) is not allowed; FORCED follows the mask spec's flags.
+ */
+int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_q,
+                           int32_t block_k, int32_t* row_ptr, int32_t* col, uint8_t* cls,
+                           int64_t capacity, int64_t* nnz_out);
+
+/*
+ * Block-sparse FlashAttention forward (prefill) on the GPU, queued on `stream`.
+ *   q   : device bf16 [B, Hq, N, d] with strides *sq (elements).
+ *   k, v: device bf16 [B, Hkv, N, d] with strides *sk, *sv. Hq % Hkv == 0.
+ *   out : device [B, Hq, N, d], bf16 or fp32 (out_dtype), strides *so.
+ *   lse : device fp32 [B, Hq, N] contiguous (natural log); may be NULL.
+ *   d   : 64 or 128. N >= 0 (any N; ragged last tiles are masked). B, Hq, Hkv >= 1.
+ *   mask, lists: the static pattern and its device block lists (see above).
+ *   tau : device fp32 [Hq], thresholds in scaled-score units (same units as s_ij);
+ *         NULL selects the dense path (every allowed tile kept, no gate evaluated).
+ *         tau = -inf keeps every tile through the gated path; NaN keeps forced tiles only.
+ *   softmax_scale: the scale in s_ij; 0 selects 1/sqrt(d).
+ *   stats   : device uint64 [B*Hq*2] = {kept, skipped} tile counts per (b, h); counts
+ *             are ADDED to the buffer (zero it first); may be NULL.
+ *   tile_max, keep: device fp32 / uint8 [B*Hq*lists->nnz], per (b, h, CSR entry) the
+ *             block maximum M_tc and the keep decision; both NULL or both set; needs
+ *             tau != NULL.
+ *   stream  : hipStream_t (NULL = default stream). The call is asynchronous.
+ * Pointers q, k, v, out must be 16-byte aligned and the n/h/b strides multiples of 8.
+ */
+int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+             const bsfa_strides* sq, const bsfa_strides* sk, const bsfa_strides* sv,
+             const bsfa_strides* so, const bsfa_mask_spec* mask,
+             const bsfa_block_lists* lists, const float* tau, float softmax_scale,
+             int32_t out_dtype, uint64_t* stats, float* tile_max, uint8_t* keep,
+             void* stream);
+
+/*
+ * Copy the per-(b, h) counters written by bsfa_fwd to the host and split them.
+ *   stats_dev: device uint64 [B*Hq*2]; kept_host, skipped_host: host uint64 [B*Hq].
+ * Synchronises `stream` before returning.
+ */
+int bsfa_skip_stats(const uint64_t* stats_dev, int32_t B, int32_t Hq, uint64_t* kept_host,
+                    uint64_t* skipped_host, void* stream);
+
+/* Thread-local text for the last failing call on this thread ("" if none). */
+const char* bsfa_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int32_t bsfa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFA_H */

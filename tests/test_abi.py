@@ -1,0 +1,110 @@
+"""The C ABI: the library loads on a CPU host, exports every declared symbol, and its
+argument checks fail cleanly (these paths return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_flashattention_amd as bsfa
+from block_sparse_flashattention_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "bsfa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|const char\*)\s+(bsfa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsfa.load_library()
+    names = _declared()
+    assert set(names) >= {"bsfa_build_block_lists", "bsfa_fwd", "bsfa_skip_stats",
+                          "bsfa_last_error", "bsfa_abi_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.bsfa_abi_version() == 1
+
+
+def test_two_call_sizing_and_too_small():
+    lib = bsfa.load_library()
+    m = binding._CMask(1, 0, 0, 1, 1)
+    nnz = ctypes.c_int64(-1)
+    row_ptr = np.zeros(17, np.int32)
+    assert lib.bsfa_build_block_lists(ctypes.byref(m), 1024, 64, 64, row_ptr.ctypes.data,
+                                      None, None, 0, ctypes.byref(nnz)) == 0
+    assert nnz.value == 136 and row_ptr[-1] == 136
+    col = np.zeros(10, np.int32)
+    cls = np.zeros(10, np.uint8)
+    rc = lib.bsfa_build_block_lists(ctypes.byref(m), 1024, 64, 64, row_ptr.ctypes.data,
+                                    col.ctypes.data, cls.ctypes.data, 10, ctypes.byref(nnz))
+    assert rc == -3 and nnz.value == 136
+    assert b"capacity" in lib.bsfa_last_error()
+
+
+def test_block_list_argument_errors():
+    lib = bsfa.load_library()
+    m = binding._CMask(1, 0, 0, 1, 1)
+    nnz = ctypes.c_int64(0)
+    assert lib.bsfa_build_block_lists(None, 64, 64, 64, None, None, None, 0, ctypes.byref(nnz)) == -1
+    assert lib.bsfa_build_block_lists(ctypes.byref(m), -1, 64, 64, None, None, None, 0, ctypes.byref(nnz)) == -1
+    assert lib.bsfa_build_block_lists(ctypes.byref(m), 64, 0, 64, None, None, None, 0, ctypes.byref(nnz)) == -1
+    bad = binding._CMask(1, -5, 0, 1, 1)
+    assert lib.bsfa_build_block_lists(ctypes.byref(bad), 64, 64, 64, None, None, None, 0, ctypes.byref(nnz)) == -1
+    assert lib.bsfa_last_error() != b""
+    # an empty sequence has no tiles
+    assert lib.bsfa_build_block_lists(ctypes.byref(m), 0, 64, 64, None, None, None, 0, ctypes.byref(nnz)) == 0
+    assert nnz.value == 0
+
+
+def _fwd_call(lib, **kw):
+    args = dict(q=16, k=16, v=16, out=16, lse=None, B=1, Hq=4, Hkv=2, N=128, d=128,
+                mask=binding._CMask(1, 0, 0, 1, 1),
+                lists=binding._CLists(2, 64, 64, 3, 16, 16, 16),
+                tau=None, scale=0.0, out_dtype=0, stats=None, tile_max=None, keep=None)
+    args.update(kw)
+    s = binding._CStrides(4 * 128 * 128, 128 * 128, 128)
+    sk = binding._CStrides(2 * 128 * 128, 128 * 128, 128)
+    return lib.bsfa_fwd(args["q"], args["k"], args["v"], args["out"], args["lse"], args["B"],
+                        args["Hq"], args["Hkv"], args["N"], args["d"], ctypes.byref(s),
+                        ctypes.byref(sk), ctypes.byref(sk), ctypes.byref(s),
+                        ctypes.byref(args["mask"]) if args["mask"] is not None else None,
+                        ctypes.byref(args["lists"]) if args["lists"] is not None else None,
+                        args["tau"], args["scale"], args["out_dtype"], args["stats"],
+                        args["tile_max"], args["keep"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=3), -1),                         # Hq not a multiple of Hkv
+    (dict(d=96), -2),                         # unsupported head dim
+    (dict(mask=None), -1),
+    (dict(lists=None), -1),
+    (dict(out_dtype=7), -1),
+    (dict(scale=-1.0), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(tile_max=16), -1),                  # tile_max without keep
+    (dict(tile_max=16, keep=16), -1),         # export without tau
+    (dict(N=129), -1),                        # lists sized for another N
+    (dict(q=None), -1),
+    (dict(q=24), -2),                         # misaligned pointer
+    (dict(B=-1), -1),
+])
+def test_fwd_argument_errors(kw, code):
+    lib = bsfa.load_library()
+    assert _fwd_call(lib, **kw) == code
+    assert lib.bsfa_last_error() != b""
+
+
+def test_fwd_empty_inputs_are_a_no_op():
+    lib = bsfa.load_library()
+    assert _fwd_call(lib, N=0, lists=binding._CLists(0, 64, 64, 0, 16, 16, 16)) == 0
+    assert _fwd_call(lib, B=0) == 0
+    assert lib.bsfa_last_error() == b""
+
+
+def test_skip_stats_argument_errors():
+    lib = bsfa.load_library()
+    assert lib.bsfa_skip_stats(None, 1, 1, 16, 16, None) == -1
+    assert lib.bsfa_skip_stats(16, 1, 0, 16, 16, None) == -1

@@ -1,0 +1,72 @@
+"""The library's analytic block classification against the oracle's element mask."""
+import itertools
+
+import numpy as np
+import pytest
+
+import block_sparse_flashattention_amd as bsfa
+from oracle import bsfa_oracle as orc
+
+SPECS = [
+    dict(causal=True, window=0, n_global=0),
+    dict(causal=False, window=0, n_global=0),
+    dict(causal=True, window=100, n_global=0),
+    dict(causal=True, window=64, n_global=64),
+    dict(causal=True, window=1024, n_global=64),
+    dict(causal=False, window=77, n_global=5),
+    dict(causal=True, window=3, n_global=1),
+    dict(causal=False, window=200, n_global=130),
+    dict(causal=True, window=0, n_global=128),
+]
+
+
+def _check(spec_kw, n, bq, bk, diag=True, glob=True):
+    m = bsfa.MaskSpec(force_keep_diag=diag, force_keep_global=glob, **spec_kw)
+    om = orc.MaskSpec(force_keep_diag=diag, force_keep_global=glob, **spec_kw)
+    row_ptr, col, cls = bsfa.build_block_lists(m, n, bq, bk)
+    nqt, nkb = -(-n // bq), -(-n // bk)
+    assert row_ptr.size == nqt + 1 and row_ptr[0] == 0 and row_ptr[-1] == col.size
+    a = orc.element_mask(np.arange(nqt * bq), np.arange(nkb * bk), n, om)
+    tiles = a.reshape(nqt, bq, nkb, bk)
+    any_allowed = tiles.any(axis=(1, 3))
+    all_allowed = tiles.all(axis=(1, 3))
+    for t in range(nqt):
+        cols = col[row_ptr[t]:row_ptr[t + 1]]
+        assert np.all(np.diff(cols) > 0)
+        assert cols.tolist() == np.nonzero(any_allowed[t])[0].tolist()
+        forced = orc.forced_tiles(t, n, om, bq, bk)
+        for e, c in zip(range(row_ptr[t], row_ptr[t + 1]), cols):
+            assert bool(cls[e] & 1) == (not all_allowed[t, c]), (t, c)
+            assert bool(cls[e] & 2) == bool(forced[c]), (t, c)
+
+
+@pytest.mark.parametrize("spec_kw", SPECS)
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 200, 640, 1000])
+def test_lists_match_element_mask_64(spec_kw, n):
+    _check(spec_kw, n, 64, 64)
+
+
+@pytest.mark.parametrize("spec_kw", SPECS[:6])
+@pytest.mark.parametrize("bq,bk", [(1, 1), (2, 3), (16, 8), (64, 32)])
+def test_lists_match_element_mask_other_blocks(spec_kw, bq, bk):
+    _check(spec_kw, 97, bq, bk)
+
+
+@pytest.mark.parametrize("diag,glob", list(itertools.product([False, True], repeat=2)))
+def test_forcing_flags(diag, glob):
+    _check(dict(causal=True, window=150, n_global=70), 500, 64, 64, diag, glob)
+
+
+def test_long_sequence_counts():
+    # causal, 64x64 tiles: allowed tiles per head = nqt (nqt + 1) / 2
+    for n in (16384, 65536):
+        row_ptr, col, cls = bsfa.build_block_lists(bsfa.MaskSpec(causal=True), n)
+        nqt = n // 64
+        assert col.size == nqt * (nqt + 1) // 2
+        assert int((cls & 2).astype(bool).sum()) == nqt  # the diagonal
+        assert int((cls & 1).astype(bool).sum()) == nqt  # only diagonal tiles are partial
+    # causal + window 1024 + 64 global tokens at N = 4096
+    row_ptr, col, cls = bsfa.build_block_lists(
+        bsfa.MaskSpec(causal=True, window=1024, n_global=64), 4096)
+    _check(dict(causal=True, window=1024, n_global=64), 4096, 64, 64)
+    assert col.size == 999

@@ -1,0 +1,112 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Every case prints its name, shape and seed before touching the GPU. Keep masks must
+match exactly except blocks whose maximum lies within 1e-3 of tau (logged); outputs
+are compared with the oracle re-run on the GPU's keep mask: max |dO| <= 1e-2,
+mean |dO| <= 1e-3, max |dLSE| <= 1e-3.
+"""
+import numpy as np
+import pytest
+
+from block_sparse_flashattention_amd import inputs
+from tests import parity_helpers as ph
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+def _case(w, tau_quantile=None, tau=None, q_tiles=None, heads=None, cal_tiles=None):
+    ph.log(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} "
+           f"causal={w.causal} window={w.window} n_global={w.n_global} seed=0")
+    if tau_quantile is not None:
+        tau = ph.oracle_tau(w, tau_quantile, q_tiles=cal_tiles)
+    qb, kb, vb = inputs.generate(w, 0)
+    res = ph.run_gpu(w, qb, kb, vb, tau)
+    rep = ph.compare(w, qb, kb, vb, res, tau, q_tiles=q_tiles, heads=heads)
+    out = res.out.float().cpu().numpy()
+    assert not np.isnan(out).any(), "an output element was never written"
+    if res.stats is not None:
+        st = res.stats.cpu().numpy()
+        nnz = res.lists.nnz
+        assert np.all(st.sum(-1) == nnz), "kept + skipped must equal the allowed tiles"
+        if res.keep is not None:
+            assert np.array_equal(st[..., 0], res.keep.cpu().numpy().astype(np.int64).sum(-1))
+    return res, rep, (qb, kb, vb), tau
+
+
+def test_single_head_1k_full():
+    w = W["single_head_1k"]
+    res, rep, _, tau = _case(w, tau_quantile=0.5)
+    skipped = res.stats.cpu().numpy()[0, 0, 1]
+    eligible = res.lists.nnz - res.lists.n_qtiles
+    ph.log(f"skipped {skipped} of {eligible} eligible tiles")
+    assert 0.3 * eligible <= skipped <= 0.7 * eligible
+
+
+def test_static_mask_4k_dense_and_gated_minus_inf():
+    w = W["static_mask_4k"]
+    res_dense, _, data, _ = _case(w, tau=None)
+    # tau = -inf through the gated kernel keeps everything and must agree bit for bit
+    res_gate = ph.run_gpu(w, *data, np.full(w.Hq, -np.inf, np.float32))
+    assert np.array_equal(res_dense.out.cpu().view(dtype=__import__("torch").int16).numpy(),
+                          res_gate.out.cpu().view(dtype=__import__("torch").int16).numpy())
+    assert np.array_equal(res_dense.lse.cpu().numpy(), res_gate.lse.cpu().numpy())
+    assert res_gate.keep.cpu().numpy().all()
+
+
+@pytest.mark.parametrize("n,hq,hkv,d,causal,window,n_global,kind", [
+    (1000, 4, 2, 128, True, 0, 0, "planted"),       # ragged tail, 2 heads per workgroup
+    (200, 2, 2, 64, False, 90, 7, "gaussian"),      # ragged, non-causal window + globals
+    (640, 8, 2, 128, True, 0, 0, "planted"),        # 4 heads per workgroup
+    (777, 3, 1, 64, True, 130, 64, "gaussian"),     # 3 query heads share one KV head
+    (64, 1, 1, 128, True, 0, 0, "gaussian"),        # a single tile
+    (1, 1, 1, 64, True, 0, 0, "gaussian"),          # a single token
+])
+def test_small_shapes(n, hq, hkv, d, causal, window, n_global, kind):
+    w = inputs.Workload(f"small_{kind}", 1, hq, hkv, n, d, causal=causal, window=window,
+                        n_global=n_global, kind=kind, planted_frac=0.1)
+    _case(w, tau_quantile=0.5)
+    _case(w, tau=None)
+
+
+def test_batch_and_fp32_output():
+    w = inputs.Workload("batch2", 2, 4, 1, 384, 128, causal=True, kind="planted",
+                        planted_frac=0.2, out_f32=True)
+    _case(w, tau_quantile=0.6)
+
+
+def test_tau_nan_and_plus_inf_keep_only_forced():
+    w = inputs.Workload("forced_only", 1, 2, 1, 512, 64, causal=True, window=200, n_global=70)
+    qb, kb, vb = inputs.generate(w, 0)
+    for val in (np.nan, np.inf):
+        tau = np.full(w.Hq, val, np.float32)
+        res = ph.run_gpu(w, qb, kb, vb, tau)
+        forced = (res.lists.cls_host & 2) != 0
+        keep = res.keep.cpu().numpy().astype(bool)
+        assert np.array_equal(keep, np.broadcast_to(forced, keep.shape))
+        ph.compare(w, qb, kb, vb, res, tau)
+
+
+def test_deterministic_run_to_run():
+    w = inputs.scaled(W["gqa_planted_16k"], N=2048)
+    qb, kb, vb = inputs.generate(w, 0)
+    tau = np.full(w.Hq, 0.5, np.float32)
+    a = ph.run_gpu(w, qb, kb, vb, tau)
+    b = ph.run_gpu(w, qb, kb, vb, tau)
+    assert np.array_equal(a.out.float().cpu().numpy(), b.out.float().cpu().numpy())
+    assert np.array_equal(a.lse.cpu().numpy(), b.lse.cpu().numpy())
+    assert np.array_equal(a.keep.cpu().numpy(), b.keep.cpu().numpy())
+
+
+def test_gqa_planted_16k_sampled():
+    """Full 16K GQA shape on the GPU; the oracle checks sampled query tiles of all heads."""
+    w = W["gqa_planted_16k"]
+    nqt = w.N // 64
+    rng = np.random.default_rng(5)
+    tiles = sorted({0, nqt - 1, *rng.choice(nqt, 3, replace=False).tolist()})
+    cal = sorted(rng.choice(nqt, 24, replace=False).tolist())
+    res, rep, _, tau = _case(w, tau_quantile=0.5, q_tiles=tiles, cal_tiles=cal)
+    st = res.stats.cpu().numpy()[0]
+    frac = st[:, 1].sum() / (st.sum() - w.Hq * nqt)
+    ph.log(f"eligible skip fraction at the calibrated tau: {frac:.3f}")
