@@ -1,0 +1,311 @@
+"""Benchmark: block-sparse FlashAttention prefill on one MI355X.
+
+Default workload: the long-context sink + local-bias GQA layer (B=1, Hq=32, Hkv=8,
+N=65536, d=128, causal, bf16), tau calibrated per head for a 50% skip of eligible
+blocks on a separate calibration seed.
+
+A "step" is one forward pass over the whole hot path: every allowed 64x64 tile gets
+its exact scores and block maximum, kept tiles get the online softmax and P.V, O and LSE
+are written once, and the per-head kept/skipped counters are updated. The static block
+lists are built once per (mask, N) and cached, as in deployment; their host build time
+is reported separately. Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (metric, value in executed TFLOP/s, roofline, cpu_baseline, ...).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+       python bench.py --copy-probe        (a plain copy of known size, for counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_flashattention_amd", "csrc", f)
+                  for f in ("bsfa_fwd.hip", "bsfa_host.cpp", "bsfa_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsfa_fwd_gated_sink_local_64k_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def tile_flops(d: int):
+    qk = 2 * 64 * 64 * d  # S = Q K^T for one 64x64 tile
+    pv = 2 * 64 * 64 * d  # O += P V for one kept tile
+    return qk, pv
+
+
+def copy_probe():
+    """One plain device copy of known size (for scaling HBM byte counters)."""
+    import torch
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes}))
+
+
+def cpu_baseline(w, taus_gpu_unused, budget_s: float = 20.0):
+    """Time the fp64 CPU oracle on a bounded, stratified sample of query tiles."""
+    from block_sparse_flashattention_amd import inputs
+    from oracle import bsfa_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    spec = orc.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
+    nqt = -(-w.N // 64)
+    heads = [(j * w.group + j % w.group) for j in range(w.Hkv)]
+    heads = [h for h in heads if h < w.Hq]
+    tiles = [int((i + 0.5) * nqt / 16) for i in range(16)]
+    groups = sorted({h // w.group for h in heads})
+    f64 = lambda bits: inputs.bits_to_f32(bits).astype(np.float64)
+    data, cal = {}, {}
+    for g in groups:
+        data[g] = inputs.generate_group(w, 0, 0, g)
+        cal[g] = inputs.generate_group(w, 1, 0, g)
+    qk_f, pv_f = tile_flops(w.d)
+    done, flop, elapsed = [], 0.0, 0.0
+    # thresholds from the oracle's own calibration (same tiles, calibration seed)
+    taus = {}
+    for h in heads:
+        g = h // w.group
+        qc = f64(cal[g][0][h - g * w.group])[None, None]
+        kc = f64(cal[g][1])[None, None]
+        taus[h] = float(orc.calibrate_tau(qc, kc, spec, 0.5, q_tiles=tiles[::4])[0])
+    order = [(t, h) for t in tiles for h in heads]
+    for t, h in order:
+        g = h // w.group
+        q = f64(data[g][0][h - g * w.group])[None, None]
+        k = f64(data[g][1])[None, None]
+        v = f64(data[g][2])[None, None]
+        t0 = time.perf_counter()
+        r = orc.attention(q, k, v, spec, tau=np.array([taus[h]]), q_tiles=[t])
+        elapsed += time.perf_counter() - t0
+        allowed = int(r.allowed.sum())
+        kept = int(r.keep.sum())
+        flop += allowed * qk_f + kept * pv_f
+        done.append((t, h))
+        if elapsed >= budget_s and len(done) >= 2:
+            break
+    return {
+        "value": flop / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(cores, blas_threads) if blas_threads > 1 else 1,
+        "kind": "oracle",
+        "sample": (f"{len(done)} (query tile, head) panels of the same workload, stratified "
+                   f"over tiles {tiles} x heads {heads}, taus from the oracle's own "
+                   f"calibration; executed FLOP counted like the GPU's; "
+                   f"{elapsed:.1f} s of fp64 numpy on {cores} visible cores, "
+                   f"BLAS threads {blas_threads}"),
+        "elapsed_s": elapsed,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sink_local_64k")
+    ap.add_argument("--quantile", type=float, default=0.5)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every calibrated quantile of the workload and tau=-inf")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+
+    import block_sparse_flashattention_amd as bsfa
+    from block_sparse_flashattention_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    mask = bsfa.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
+    out_dtype = torch.float32 if w.out_f32 else torch.bfloat16
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.perf_counter()
+    qb, kb, vb = inputs.generate(w, 0)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    del qb, kb, vb
+    qc, kc, _ = inputs.generate(w, 1)
+    qc_d, kc_d = to_dev(qc), to_dev(kc)
+    del qc, kc
+    log(f"[bench] inputs generated and resident in {time.perf_counter() - t0:.1f} s")
+
+    t0 = time.perf_counter()
+    row_ptr, col, cls = bsfa.build_block_lists(mask, w.N)
+    lists_host_s = time.perf_counter() - t0
+    lists = bsfa.BlockLists.get(mask, w.N, dev)
+
+    quantiles = sorted(set([args.quantile] + (list(w.tau_quantiles) if args.sweep else [])))
+    taus = bsfa.calibrate_tau(qc_d, kc_d, mask, quantiles)
+    del qc_d, kc_d
+    torch.cuda.synchronize()
+    log(f"[bench] calibrated tau for quantiles {quantiles}")
+
+    out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=out_dtype, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stats = torch.zeros((w.B, w.Hq, 2), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(tau_t):
+        stats.zero_()
+        bsfa.fwd(q, k, v, mask=mask, tau=tau_t, out=out, lse_out=lse, stats_out=stats,
+                 lists=lists, stream=stream.cuda_stream)
+
+    def timed(tau_t, label):
+        for _ in range(args.warmup):
+            step(tau_t)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t_start = time.perf_counter()
+        for s, e in evs:
+            stats.zero_()
+            s.record(stream)
+            bsfa.fwd(q, k, v, mask=mask, tau=tau_t, out=out, lse_out=lse, stats_out=stats,
+                     lists=lists, stream=stream.cuda_stream)
+            e.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        kern_ms = [s.elapsed_time(e) for s, e in evs]
+        st = stats.cpu().numpy()
+        log(f"[bench] {label}: {wall / args.steps * 1e3:.3f} ms/step, kernel mean "
+            f"{np.mean(kern_ms):.3f} ms (min {np.min(kern_ms):.3f})")
+        return wall / args.steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms)), st
+
+    qk_f, pv_f = tile_flops(w.d)
+    allowed_tiles = lists.nnz * w.B * w.Hq
+    forced_tiles = int(((cls & 2) != 0).sum()) * w.B * w.Hq
+    dense_flop = allowed_tiles * (qk_f + pv_f)
+    alg_bytes = (2 * w.B * w.Hq * w.N * w.d * 2 + 2 * w.B * w.Hkv * w.N * w.d * 2
+                 + w.B * w.Hq * w.N * 4) + (2 * w.B * w.Hq * w.N * w.d if w.out_f32 else 0)
+
+    dense_ms, dense_kern, _, _ = timed(None, "dense path (tau=NULL)")
+
+    results = {}
+    for qi, qv in enumerate(quantiles):
+        tau_t = torch.tensor(taus[qi], dtype=torch.float32, device=dev)
+        ms, kern, kern_med, st = timed(tau_t, f"gated tau@q={qv}")
+        kept, skipped = int(st[..., 0].sum()), int(st[..., 1].sum())
+        exec_flop = kept * (qk_f + pv_f) + skipped * qk_f
+        results[qv] = dict(ms=ms, kernel_ms=kern, kernel_ms_median=kern_med, kept=kept,
+                           skipped=skipped, exec_flop=exec_flop,
+                           skip_eligible=skipped / max(allowed_tiles - forced_tiles, 1),
+                           skip_allowed=skipped / max(allowed_tiles, 1))
+    gate_ms = None
+    if args.sweep:
+        gate_ms, _, _, _ = timed(torch.full((w.Hq,), -math.inf, device=dev), "gated tau=-inf")
+
+    head = results[args.quantile]
+    value = head["exec_flop"] / (head["ms"] / 1e3) / 1e12
+    achieved = head["exec_flop"] / (head["kernel_ms"] / 1e3) / 1e12
+    line = {
+        "metric": "BSFA prefill executed TFLOP/s (bf16 MFMA), % of MFMA peak, speedup vs dense path",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "mask": ("causal" if w.causal else "full")
+                           + (f"+window{w.window}" if w.window else "")
+                           + (f"+global{w.n_global}" if w.n_global else ""),
+                   "tau_quantile": args.quantile, "block": "64x64",
+                   "out_dtype": "f32" if w.out_f32 else "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic()},
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "dense_equiv_tflops": round(dense_flop / (head["ms"] / 1e3) / 1e12, 2),
+        "dense_path_ms": round(dense_ms, 4),
+        "dense_path_tflops": round(dense_flop / (dense_ms / 1e3) / 1e12, 2),
+        "speedup_vs_dense": round(dense_ms / head["ms"], 4),
+        "skip_fraction_eligible": round(head["skip_eligible"], 4),
+        "skip_fraction_allowed": round(head["skip_allowed"], 4),
+        "kernel_ms_mean": round(head["kernel_ms"], 4),
+        "hbm_algorithmic_gbs": round(alg_bytes / (head["kernel_ms"] / 1e3) / 1e9, 1),
+        "block_lists_host_ms": round(lists_host_s * 1e3, 2),
+        "executed_flop_per_step": head["exec_flop"],
+        "dense_flop_per_step": dense_flop,
+    }
+    if args.sweep:
+        line["sweep"] = {str(qv): {"ms": round(r["ms"], 4),
+                                   "exec_tflops": round(r["exec_flop"] / (r["ms"] / 1e3) / 1e12, 2),
+                                   "speedup_vs_dense": round(dense_ms / r["ms"], 4),
+                                   "skip_fraction_eligible": round(r["skip_eligible"], 4)}
+                         for qv, r in results.items()}
+        line["gated_tau_minus_inf_ms"] = round(gate_ms, 4)
+    if not args.no_cpu_baseline:
+        del q, k, v, out, lse
+        torch.cuda.empty_cache()
+        log("[bench] timing the CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(w, taus, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,13 +173,15 @@ def _strides(t) -> _CStrides:
 
 def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0.0,
         out_dtype=None, out=None, want_lse: bool = True, stats: bool = False,
-        export_tiles: bool = False, lists: BlockLists | None = None, stream=None) -> FwdResult:
+        export_tiles: bool = False, lists: BlockLists | None = None, stream=None,
+        lse_out=None, stats_out=None) -> FwdResult:
     """Block-sparse attention forward on the GPU (asynchronous on the current stream).
 
     q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d] (CUDA/HIP tensors, last dim
     contiguous). tau: None (dense path) or fp32 tensor [Hq] on the device (or anything
     torch.as_tensor accepts). Returns out [B, Hq, N, d] (bf16 or fp32), lse fp32
     [B, Hq, N], optional per-(b, h) {kept, skipped} counts and per-tile export.
+    ``lse_out`` / ``stats_out`` reuse caller buffers (stats are added to stats_out).
     """
     import torch
 
@@ -197,7 +199,10 @@ def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0
         out_dtype = torch.bfloat16
     if out is None:
         out = torch.empty((bsz, hq, n, d), dtype=out_dtype, device=dev)
-    lse = torch.empty((bsz, hq, n), dtype=torch.float32, device=dev) if want_lse else None
+    if lse_out is not None:
+        lse = lse_out
+    else:
+        lse = torch.empty((bsz, hq, n), dtype=torch.float32, device=dev) if want_lse else None
     if lists is None:
         lists = BlockLists.get(mask, n, dev)
     tau_t = None
@@ -208,7 +213,10 @@ def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0
         if tau_t.numel() != hq:
             raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
         tau_t = tau_t.contiguous()
-    st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
+    if stats_out is not None:
+        st = stats_out
+    else:
+        st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
     tm = kp = None
     if export_tiles:
         tm = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.float32, device=dev)
@@ -249,10 +257,14 @@ def skip_stats(stats_tensor, stream=None):
     return kept, skipped
 
 
-def calibrate_tau(q, k, mask: MaskSpec, quantile: float, softmax_scale: float = 0.0):
-    """Per-head threshold: the ``quantile`` of the eligible (allowed, not forced) block
-    maxima of each query head, measured on calibration inputs q, k with the gated kernel
-    at tau = -inf (nothing skipped) and its per-tile export. Returns fp32 numpy [Hq]."""
+def calibrate_tau(q, k, mask: MaskSpec, quantile, softmax_scale: float = 0.0):
+    """One-time per-head threshold calibration (Block Sparse Flash Attention, "The
+    paper's improvements": thresholds learned once per layer and head on a small data set).
+
+    tau_h = the ``quantile`` of the eligible (allowed, not forced) block maxima of query
+    head h on calibration inputs q, k, measured with the gated kernel at tau = -inf
+    (nothing skipped) and its per-tile export. ``quantile`` may be a scalar (returns fp32
+    [Hq]) or a sequence (returns fp32 [len(quantile), Hq])."""
     import torch
 
     hq = q.shape[1]
@@ -260,8 +272,9 @@ def calibrate_tau(q, k, mask: MaskSpec, quantile: float, softmax_scale: float = 
               softmax_scale=softmax_scale, want_lse=False, export_tiles=True)
     tmax = res.tile_max.float().cpu().numpy()  # [B, Hq, nnz]
     eligible = (res.lists.cls_host & BSFA_CLS_FORCED) == 0
-    taus = np.empty(hq, dtype=np.float32)
+    qs = np.atleast_1d(np.asarray(quantile, dtype=np.float64))
+    taus = np.empty((qs.size, hq), dtype=np.float32)
     for h in range(hq):
         vals = tmax[:, h, :][:, eligible].reshape(-1)
-        taus[h] = np.quantile(vals, quantile) if vals.size else -np.inf
-    return taus
+        taus[:, h] = np.quantile(vals, qs) if vals.size else -np.inf
+    return taus[0] if np.ndim(quantile) == 0 else taus

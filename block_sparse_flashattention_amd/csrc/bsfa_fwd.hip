@@ -118,8 +118,14 @@ struct TileIO {
   }
 };
 
-template <int D, int HPACK, bool SKIP, bool OUT_F32>
+// Kernel modes: the dense path (no gate), the gated path, and the gated path that also
+// exports every tile's maximum and keep bit (calibration and parity checks).
+enum Mode { DENSE = 0, GATED = 1, GATED_EXPORT = 2 };
+
+template <int D, int HPACK, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) {
+  constexpr bool SKIP = MODE != DENSE;
+  constexpr bool EXPORT = MODE == GATED_EXPORT;
   constexpr int NW = 2 * HPACK;  // waves per workgroup
   constexpr int NT = 64 * NW;    // threads per workgroup
   constexpr int KS = D / 16;     // 16-wide steps along d for S^T = K Q^T
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
       }
     }
     if (keep_h) ++n_kept; else ++n_skip;
-    if (SKIP && a.tile_max && (wave & 1) == 0 && lane == 0) {
+    if (EXPORT && (wave & 1) == 0 && lane == 0) {
       const int64_t idx = ((int64_t)b * a.Hq + hq) * a.nnz + e;
       a.tile_max[idx] = tmax_h;
       a.keep[idx] = keep_h ? 1 : 0;
@@ -356,22 +362,25 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
   }
 }
 
-template <int D, int HPACK, bool SKIP, bool OUT_F32>
+template <int D, int HPACK, int MODE, bool OUT_F32>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * (a.Hq / HPACK) * a.nqt);
-  hipLaunchKernelGGL((bsfa_fwd_kernel<D, HPACK, SKIP, OUT_F32>), dim3(grid), dim3(128 * HPACK),
+  hipLaunchKernelGGL((bsfa_fwd_kernel<D, HPACK, MODE, OUT_F32>), dim3(grid), dim3(128 * HPACK),
                      0, stream, a);
   return hipGetLastError();
 }
 
+template <int D, int HPACK, int MODE>
+hipError_t launch_mode(const FwdArgs& a, bool out_f32, hipStream_t s) {
+  return out_f32 ? launch_variant<D, HPACK, MODE, true>(a, s)
+                 : launch_variant<D, HPACK, MODE, false>(a, s);
+}
+
 template <int D, int HPACK>
 hipError_t launch_hpack(const FwdArgs& a, bool out_f32, hipStream_t s) {
-  const bool skip = a.tau != nullptr;
-  if (skip)
-    return out_f32 ? launch_variant<D, HPACK, true, true>(a, s)
-                   : launch_variant<D, HPACK, true, false>(a, s);
-  return out_f32 ? launch_variant<D, HPACK, false, true>(a, s)
-                 : launch_variant<D, HPACK, false, false>(a, s);
+  if (a.tau == nullptr) return launch_mode<D, HPACK, DENSE>(a, out_f32, s);
+  if (a.tile_max != nullptr) return launch_mode<D, HPACK, GATED_EXPORT>(a, out_f32, s);
+  return launch_mode<D, HPACK, GATED>(a, out_f32, s);
 }
 
 template <int D>
