@@ -76,44 +76,57 @@ __device__ __forceinline__ void pair32(float x, float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bool allowed(int i, int j, int n, int causal, int window, int ng) {
-  if (i >= n || j >= n) return false;
-  if (causal && j > i) return false;
-  if (window > 0) {
-    const int dist = i > j ? i - j : j - i;
-    if (!(dist < window || j < ng || i < ng)) return false;
-  }
-  return true;
+// Read-only kernel inputs (block lists, thresholds) are read through the constant
+// address space: with a wave-uniform index they become scalar loads, which wait on
+// their own counter instead of the vector-memory counter the K/V prefetch uses.
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)(p))[i];
 }
 
-template <int D, int NT>
-struct TileIO {
-  static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int CPT = BLK * CPR / NT;     // chunks per thread
-  static_assert(BLK * CPR % NT == 0, "tile chunks must divide evenly");
+// Byte i of a 4-byte aligned byte array, read as its aligned dword (a scalar load).
+__device__ __forceinline__ int ldc_byte(const uint8_t* p, int64_t i) {
+  const uint32_t w = ldc(reinterpret_cast<const uint32_t*>(p), i >> 2);
+  return (int)((w >> (8 * (i & 3))) & 0xFFu);
+}
 
-  // Rows [c*64, c*64+64) of a [N, D] bf16 matrix (row stride sn) into registers;
-  // rows at or past n read as zeros.
+__device__ __forceinline__ bool allowed(int i, int j, int n, int causal, int window, int ng) {
+  // branch-free: bitwise combination of the static primitives
+  const int dist = i > j ? i - j : j - i;
+  const bool inside = (i < n) & (j < n);
+  const bool causal_ok = (causal == 0) | (j <= i);
+  const bool pattern = (window <= 0) | (dist < window) | (j < ng) | (i < ng);
+  return inside & causal_ok & pattern;
+}
+
+// LDS tiles are 64 rows x D bf16 with padded rows: K rows are D + 8 elements apart
+// (16 consecutive rows at one column hit 16 distinct bank groups), V rows D + 16 (the
+// four rows x 32 bytes of a 16-lane transpose read hit distinct banks). Every read then
+// uses one per-lane base address plus immediate offsets. Tiles are staged through
+// registers (coalesced 16-byte global loads, then 16-byte LDS writes).
+template <int D, int NT>
+struct Stage {
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int CPT = BLK * CPR / NT;  // chunks per thread
+  static_assert(BLK * CPR % NT == 0, "tile chunks must divide evenly");
+  // Rows [c*64, c*64+64) of a [N, D] matrix; rows past N are clamped to row N-1 (finite
+  // values whose scores are masked and whose weights are zero).
   __device__ __forceinline__ static void load(u32x4_t (&r)[CPT], const uint16_t* base,
-                                              int64_t sn, int c, int n, int tid) {
+                                              int64_t sn, int c, int nmax, int tid) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int key = c * BLK + row;
-      if (c >= 0 && key < n)
-        r[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)key * sn + cc * 8);
-      else
-        r[i] = u32x4_t{0u, 0u, 0u, 0u};
+      int key = c * BLK + ch / CPR;
+      key = key < 0 ? 0 : (key > nmax ? nmax : key);
+      r[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)key * sn + (ch % CPR) * 8);
     }
   }
-  template <int ROWSTRIDE>
-  __device__ __forceinline__ static void store(uint16_t* s, const u32x4_t (&r)[CPT], int tid) {
+  template <int ROW>
+  __device__ __forceinline__ static void store(uint16_t* tile, const u32x4_t (&r)[CPT], int tid) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT;
-      const int row = ch / CPR, cc = ch % CPR;
-      *reinterpret_cast<u32x4_t*>(s + row * ROWSTRIDE + cc * 8) = r[i];
+      *reinterpret_cast<u32x4_t*>(tile + (ch / CPR) * ROW + (ch % CPR) * 8) = r[i];
     }
   }
 };
@@ -122,21 +135,28 @@ struct TileIO {
 // exports every tile's maximum and keep bit (calibration and parity checks).
 enum Mode { DENSE = 0, GATED = 1, GATED_EXPORT = 2 };
 
+// Software pipeline over the query tile's block list (one tile of lag):
+//   iteration e:  barrier (K(e+1), V(e) staged)
+//                 issue K(e+2) loads
+//                 softmax(e) -> P(e) in bf16          | QK^T(e+1) -> S(e+1), block max
+//                 barrier; gate(e+1); issue V(e+1) loads only if some head keeps e+1
+//                 O += P(e) V(e)
+// so V(e+1)'s load latency is covered by P.V(e), and K(e+2)'s by a whole iteration.
 template <int D, int HPACK, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) {
-  constexpr bool SKIP = MODE != DENSE;
+  constexpr bool GATE = MODE != DENSE;
   constexpr bool EXPORT = MODE == GATED_EXPORT;
   constexpr int NW = 2 * HPACK;  // waves per workgroup
-  constexpr int NT = 64 * NW;    // threads per workgroup
   constexpr int KS = D / 16;     // 16-wide steps along d for S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row tiles of O^T along d
-  constexpr int KROW = D + 8;    // K tile row stride in LDS (elements): +16 B pad
-  constexpr int VROW = D + 16;   // V tile row stride in LDS (elements): +32 B pad
-  using IO = TileIO<D, NT>;
+  constexpr int NT = 64 * NW;
+  constexpr int KROW = D + 8;   // K tile row stride (elements)
+  constexpr int VROW = D + 16;  // V tile row stride (elements)
+  using ST = Stage<D, NT>;
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BLK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BLK * VROW];
-  __shared__ float sRed[NW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BLK * VROW];
+  __shared__ float sRed[2][NW];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -179,49 +199,32 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
 
   float tau_pack[HPACK];
 #pragma unroll
-  for (int j = 0; j < HPACK; ++j) tau_pack[j] = SKIP ? a.tau[hp * HPACK + j] : 0.0f;
+  for (int j = 0; j < HPACK; ++j) tau_pack[j] = GATE ? ldc(a.tau, hp * HPACK + j) : 0.0f;
 
-  int e0 = a.row_ptr[t], e1 = a.row_ptr[t + 1];
+  int e0 = ldc(a.row_ptr, t), e1 = ldc(a.row_ptr, t + 1);
   e0 = e0 < 0 ? 0 : (e0 > a.nnz ? (int)a.nnz : e0);
   e1 = e1 < e0 ? e0 : (e1 > a.nnz ? (int)a.nnz : e1);
 
   const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)g * a.skh;
   const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)g * a.svh;
+  const int nmax = a.N - 1;
 
-  float m_run = -INFINITY;  // running max of raw q.k over kept keys of this row
-  float l_run = 0.0f;       // this lane's share of the running sum
-  f32x16_t o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
-  unsigned n_kept = 0, n_skip = 0;
-
-  u32x4_t kr[IO::CPT], vr[IO::CPT];
-  if (e0 < e1) {
-    IO::load(kr, kbase, a.skn, a.col[e0], a.N, tid);
-    IO::template store<KROW>(sK[0], kr, tid);
-  }
-
-  for (int e = e0; e < e1; ++e) {
-    const int buf = (e - e0) & 1;
-    const int c = a.col[e];
-    const int cls = a.cls[e];
-    const bool has_next = e + 1 < e1;
-    if (has_next) IO::load(kr, kbase, a.skn, a.col[e + 1], a.N, tid);
-    __syncthreads();  // K(e) staged; every wave is done with iteration e-1
-
-    // ---- S^T = K(e) Q^T for this wave's 32 queries: two 32x32 key tiles
-    f32x16_t s[2];
+  // S^T = K(tile) Q^T for this wave's 32 queries: two 32x32 key tiles.
+  auto qk = [&](const uint16_t* tile, f32x16_t (&s)[2]) {
     s[0] = f32x16_t{};
     s[1] = f32x16_t{};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            &sK[buf][(mt * 32 + l32) * KROW + ks * 16 + half * 8]);
+            tile + (mt * 32 + l32) * KROW + ks * 16 + half * 8);
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
       }
-    }
+  };
+
+  // Mask a PARTIAL tile element-wise and return this lane's maximum (raw units).
+  auto mask_max = [&](f32x16_t (&s)[2], int c, int cls) -> float {
     if (cls & BSFA_CLS_PARTIAL) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -236,89 +239,164 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
+    return mx;
+  };
 
-    bool keep_h = true, any_keep = true;
-    float tmax_h = 0.0f;
-    if constexpr (SKIP) {
-      const float wm = wave_max(mx);
-      if (lane == 0) sRed[wave] = wm;
-      if (has_next) IO::template store<KROW>(sK[buf ^ 1], kr, tid);
-      __syncthreads();  // block maxima of every wave visible
-      const bool forced = (cls & BSFA_CLS_FORCED) != 0;
-      any_keep = false;
+  // The gate: block maxima of every wave to LDS, one barrier, then per-head decisions.
+  auto gate = [&](float mx, int slot, int cls, bool& keep_h, bool& any_keep, float& tmax_h) {
+    const float wm = wave_max(mx);
+    if (lane == 0) sRed[slot][wave] = wm;
+    __syncthreads();
+    const bool forced = (cls & BSFA_CLS_FORCED) != 0;
+    any_keep = false;
 #pragma unroll
-      for (int j = 0; j < HPACK; ++j) {
-        const float tm = fmaxf(sRed[2 * j], sRed[2 * j + 1]) * a.scale;
-        const bool kj = forced || (tm >= tau_pack[j]);
-        if (j == (wave >> 1)) {
-          keep_h = kj;
-          tmax_h = tm;
-        }
-        any_keep = any_keep || kj;
+    for (int j = 0; j < HPACK; ++j) {
+      const float tm = fmaxf(sRed[slot][2 * j], sRed[slot][2 * j + 1]) * a.scale;
+      const bool kj = forced || (tm >= tau_pack[j]);
+      if (j == (wave >> 1)) {
+        keep_h = kj;
+        tmax_h = tm;
       }
+      any_keep = any_keep || kj;
+    }
+  };
+
+  float m_run = -INFINITY;  // reference max (raw q.k units) of this lane's row
+  float l_run = 0.0f;       // this lane's share of sum exp(scale * (s - m_run))
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
+  unsigned n_kept = 0, n_skip = 0;
+
+  f32x16_t s_cur[2];
+  float mx_cur = -INFINITY, tmax_cur = 0.0f;
+  bool keep_cur = false, any_cur = false;
+
+  // Register staging: kr holds K(e+2) and vr holds V(e+1) while iteration e runs.
+  u32x4_t kr[ST::CPT], vr[ST::CPT];
+  if (e0 < e1) {
+    ST::load(kr, kbase, a.skn, ldc(a.col, e0), nmax, tid);
+    ST::template store<KROW>(sK[0], kr, tid);
+    if (e0 + 1 < e1) {
+      ST::load(kr, kbase, a.skn, ldc(a.col, e0 + 1), nmax, tid);
+      ST::template store<KROW>(sK[1], kr, tid);
+    }
+    __syncthreads();
+    qk(sK[0], s_cur);
+    mx_cur = mask_max(s_cur, ldc(a.col, e0), ldc_byte(a.cls, e0));
+    if constexpr (GATE) {
+      gate(mx_cur, 0, ldc_byte(a.cls, e0), keep_cur, any_cur, tmax_cur);
     } else {
-      if (has_next) IO::template store<KROW>(sK[buf ^ 1], kr, tid);
+      keep_cur = any_cur = true;
+    }
+    if (any_cur) {
+      ST::load(vr, vbase, a.svn, ldc(a.col, e0), nmax, tid);
+      ST::template store<VROW>(sV[0], vr, tid);
+    }
+    if (e0 + 2 < e1) ST::load(kr, kbase, a.skn, ldc(a.col, e0 + 2), nmax, tid);
+    if (!GATE && e0 + 1 < e1) ST::load(vr, vbase, a.svn, ldc(a.col, e0 + 1), nmax, tid);
+  }
+
+  const float c2 = a.scale_log2;
+  for (int e = e0; e < e1; ++e) {
+    const int i = e - e0;
+    const bool has_next = e + 1 < e1;
+    __syncthreads();  // K(e+1) in sK[(i+1)&1], V(e) in sV[i&1]; iteration e-1 finished
+
+    // ---- softmax of tile e (kept tiles only): P in bf16, running max/sum update.
+    // The reference max is raised only when some row's max grows by more than 2^8 in
+    // exp2 units (or on a row's first keys), so P <= 256 and O rarely needs rescaling.
+    bf16x8_t pb[4];
+    bool rescale = false;
+    float alpha = 1.0f;
+    if (keep_cur) {
+      float x0, x1;
+      pair32(mx_cur, x0, x1);
+      const float m_new = fmaxf(m_run, fmaxf(x0, x1));
+      const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY)
+                                             : ((m_new - m_run) * c2 > 8.0f);
+      rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+      if (rescale) {
+        alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+        m_run = m_new;
+        l_run *= alpha;
+      }
+      const float mb = (m_run == -INFINITY ? 0.0f : m_run) * c2;
+      float rs = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s_cur[ks >> 1][8 * (ks & 1) + j], c2, -mb));
+          rs += pv;
+          pb[ks][j] = (__bf16)pv;
+        }
+      l_run += rs;
     }
 
-    if (any_keep) {
-      IO::load(vr, vbase, a.svn, c, a.N, tid);
-      IO::template store<VROW>(sV, vr, tid);
-      __syncthreads();  // V(e) staged
-      if (keep_h) {
-        // ---- online softmax for this lane's query row (raw-score units)
-        float x0, x1;
-        pair32(mx, x0, x1);
-        const float m_new = fmaxf(m_run, fmaxf(x0, x1));
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.scale_log2);
-        const float mb = m_use * a.scale_log2;
-        float rs = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][i], a.scale_log2, -mb));
-            s[mt][i] = pv;
-            rs += pv;
-          }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+    // ---- scores and block maximum of tile e+1
+    f32x16_t s_nxt[2];
+    float mx_nxt = -INFINITY, tmax_nxt = 0.0f;
+    bool keep_nxt = true, any_nxt = true;
+    if (has_next) {
+      qk(sK[(i + 1) & 1], s_nxt);
+      mx_nxt = mask_max(s_nxt, ldc(a.col, e + 1), ldc_byte(a.cls, e + 1));
+      if constexpr (GATE) {
+        gate(mx_nxt, (i + 1) & 1, ldc_byte(a.cls, e + 1), keep_nxt, any_nxt, tmax_nxt);
+        if (any_nxt) ST::load(vr, vbase, a.svn, ldc(a.col, e + 1), nmax, tid);
+      }
+    }
+
+    // ---- O^T += V(e)^T P(e)^T
+    if (keep_cur) {
+      if (rescale) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-
-        // ---- O^T += V^T P^T
-        const int vrow = 4 * half + ((lane & 15) >> 2);
-        const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      // V^T operand via ds_read_tr16_b64: lane (half h, in-group index jl) addresses
+      // row 16*ks + 4*h + jl/4 (+8 for the second read), column 32*dt + 16*((lane/16)%2)
+      // + 4*(jl%4); all (ks, dt) steps are immediate offsets from one base.
+      const int jl = lane & 15;
+      const uint16_t* vt = sV[i & 1] + (4 * half + (jl >> 2)) * VROW + 16 * ((lane >> 4) & 1) +
+                           4 * (jl & 3);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bf16x8_t pb;
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[ks >> 1][8 * (ks & 1) + j];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* p0 = &sV[(16 * ks + vrow) * VROW + 32 * dt + vcol];
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t*)(p0));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t*)(p0 + 8 * VROW));
-            // Whole-vector concatenation and bit cast: an element-by-element copy from
-            // the two i16x4 results into a bf16x8 is lowered with a wrong v_perm_b32
-            // (it duplicated element 0) by this compiler.
-            const i16x8_t cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, cat);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-          }
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* p0 = vt + 16 * ks * VROW + 32 * dt;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(p0));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(p0 + 8 * VROW));
+          // Whole-vector concatenation and bit cast: an element-by-element copy from
+          // the two i16x4 results into a bf16x8 is lowered with a wrong v_perm_b32
+          // (it duplicated element 0) by this compiler.
+          const i16x8_t cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, cat);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[dt], 0, 0, 0);
         }
       }
     }
-    if (keep_h) ++n_kept; else ++n_skip;
+    if (keep_cur) ++n_kept; else ++n_skip;
     if (EXPORT && (wave & 1) == 0 && lane == 0) {
       const int64_t idx = ((int64_t)b * a.Hq + hq) * a.nnz + e;
-      a.tile_max[idx] = tmax_h;
-      a.keep[idx] = keep_h ? 1 : 0;
+      a.tile_max[idx] = tmax_cur;
+      a.keep[idx] = keep_cur ? 1 : 0;
     }
+    // Stage K(e+2) and V(e+1) (loads issued one iteration / one P.V earlier); their
+    // buffers were last read in iteration e-1, and the next barrier publishes them.
+    if (e + 2 < e1) ST::template store<KROW>(sK[i & 1], kr, tid);
+    if (has_next && any_nxt) ST::template store<VROW>(sV[(i + 1) & 1], vr, tid);
+    if (e + 3 < e1) ST::load(kr, kbase, a.skn, ldc(a.col, e + 3), nmax, tid);
+    if (!GATE && e + 2 < e1) ST::load(vr, vbase, a.svn, ldc(a.col, e + 2), nmax, tid);
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
+    mx_cur = mx_nxt;
+    tmax_cur = tmax_nxt;
+    keep_cur = keep_nxt;
+    any_cur = any_nxt;
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale * m + ln l; one store per element

@@ -151,6 +151,8 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   if (!q || !k || !v || !out) return fail(BSFA_ERR_INVALID_ARG, "q, k, v, out are required");
   if (!lists->row_ptr || (lists->nnz > 0 && (!lists->col || !lists->cls)))
     return fail(BSFA_ERR_INVALID_ARG, "block list arrays missing");
+  if (((uintptr_t)lists->row_ptr | (uintptr_t)lists->col | (uintptr_t)lists->cls) & 3u)
+    return fail(BSFA_ERR_UNSUPPORTED, "block list arrays must be 4-byte aligned");
   if (!sq || !sk || !sv || !so) return fail(BSFA_ERR_INVALID_ARG, "strides are required");
   if (!valid_strides(sq) || !valid_strides(sk) || !valid_strides(sv) || !valid_strides(so))
     return fail(BSFA_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");

@@ -82,7 +82,10 @@ typedef struct {
  * owns entries [row_ptr[t], row_ptr[t+1]), each a key block index col[e] (ascending)
  * and a class cls[e] (BSFA_CLS_* flags). Tiles with no allowed element are absent.
  * For bsfa_fwd the three arrays are in device memory and must come from
- * bsfa_build_block_lists for the same mask spec, N and 64x64 blocks.
+ * bsfa_build_block_lists for the same mask spec, N and 64x64 blocks. Each array must be
+ * 4-byte aligned, and cls must stay readable up to the next 4-byte boundary past its
+ * last entry (the kernel reads it as aligned 32-bit words; any hipMalloc allocation
+ * satisfies this).
  */
 typedef struct {
   int32_t n_qtiles; /* ceil(N / block_q)                    */
