@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/bsfa.h"
 #include "bsfa_internal.h"
 
@@ -99,30 +101,41 @@ __device__ __forceinline__ bool allowed(int i, int j, int n, int causal, int win
   return inside & causal_ok & pattern;
 }
 
-// LDS tiles are 64 rows x D bf16 with padded rows: K rows are D + 8 elements apart
-// (16 consecutive rows at one column hit 16 distinct bank groups), V rows D + 16 (the
-// four rows x 32 bytes of a 16-lane transpose read hit distinct banks). Every read then
-// uses one per-lane base address plus immediate offsets. Tiles are staged through
-// registers (coalesced 16-byte global loads, then 16-byte LDS writes).
+// LDS tiles are 64 rows x D bf16 with padded rows. K rows are D + 8 elements apart, so
+// 16 consecutive rows at one column hit 16 distinct 4-bank groups. V rows are D + 32
+// elements apart, so the four rows x 64 bytes that 32 lanes of a transpose read touch
+// cover all 64 banks once. Every LDS read is one per-lane base address plus immediate
+// offsets.
+//
+// K/V tiles are staged through registers with bounds-checked buffer loads: one 16-byte
+// chunk per lane and instruction, with the tile's offset as the scalar offset, so the
+// address math is a single scalar multiply per tile. A row at or past N reads as zeros
+// (its scores are masked and its weights are zero).
 template <int D, int NT>
 struct Stage {
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int CPT = BLK * CPR / NT;  // chunks per thread
   static_assert(BLK * CPR % NT == 0, "tile chunks must divide evenly");
-  // Rows [c*64, c*64+64) of a [N, D] matrix; rows past N are clamped to row N-1 (finite
-  // values whose scores are masked and whose weights are zero).
-  __device__ __forceinline__ static void load(u32x4_t (&r)[CPT], const uint16_t* base,
-                                              int64_t sn, int c, int nmax, int tid) {
+  uint32_t goff[CPT];  // byte offset of this thread's chunks inside a tile (global)
+
+  __device__ __forceinline__ void init(int tid, int64_t sn) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT;
-      int key = c * BLK + ch / CPR;
-      key = key < 0 ? 0 : (key > nmax ? nmax : key);
-      r[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)key * sn + (ch % CPR) * 8);
+      goff[i] = (uint32_t)((ch / CPR) * sn * 2 + (ch % CPR) * 16);
     }
   }
+  __device__ __forceinline__ void load(u32x4_t (&r)[CPT], __amdgpu_buffer_rsrc_t rsrc,
+                                       uint32_t tile_off) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      r[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc, goff[i], tile_off, 0));
+  }
+  // Write the chunks into an LDS tile whose rows are ROW elements apart.
   template <int ROW>
-  __device__ __forceinline__ static void store(uint16_t* tile, const u32x4_t (&r)[CPT], int tid) {
+  __device__ __forceinline__ static void store(uint16_t* tile, const u32x4_t (&r)[CPT],
+                                               int tid) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * NT;
@@ -135,31 +148,43 @@ struct Stage {
 // exports every tile's maximum and keep bit (calibration and parity checks).
 enum Mode { DENSE = 0, GATED = 1, GATED_EXPORT = 2 };
 
-// Software pipeline over the query tile's block list (one tile of lag):
-//   iteration e:  barrier (K(e+1), V(e) staged)
-//                 issue K(e+2) loads
-//                 softmax(e) -> P(e) in bf16          | QK^T(e+1) -> S(e+1), block max
-//                 barrier; gate(e+1); issue V(e+1) loads only if some head keeps e+1
-//                 O += P(e) V(e)
-// so V(e+1)'s load latency is covered by P.V(e), and K(e+2)'s by a whole iteration.
+struct TileState {
+  float mx;    // this lane's maximum of the tile's raw scores
+  float tmax;  // the head's block maximum in scaled units (gated modes)
+  bool keep;   // this head keeps the tile
+  bool any;    // some head of the workgroup keeps it (its V block is loaded)
+};
+
+// Software pipeline over the query tile's block list, one barrier per tile. Step e:
+//   S(e+1) = K(e+1) Q^T interleaved with P(e) = exp(S(e) - m)   (K(e+1) already staged)
+//   block max of S(e+1) -> LDS; V(e) and K(e+2) registers -> LDS
+//   barrier
+//   gate(e+1)
+//   O += P(e) V(e)
+//   issue loads of V(e+1) (only if some head keeps e+1) and K(e+3)
+// so each load's latency is covered by the next step's QK^T/softmax block, and the
+// staging registers are free while P.V runs.
 template <int D, int HPACK, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) {
   constexpr bool GATE = MODE != DENSE;
   constexpr bool EXPORT = MODE == GATED_EXPORT;
   constexpr int NW = 2 * HPACK;  // waves per workgroup
+  constexpr int NT = 64 * NW;
   constexpr int KS = D / 16;     // 16-wide steps along d for S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row tiles of O^T along d
-  constexpr int NT = 64 * NW;
-  constexpr int KROW = D + 8;   // K tile row stride (elements)
-  constexpr int VROW = D + 16;  // V tile row stride (elements)
-  using ST = Stage<D, NT>;
+  constexpr int KROW = D + 8;    // K tile row stride (elements)
+  constexpr int VROW = D + 32;   // V tile row stride (elements)
+  constexpr int NQK = 2 * KS;    // MFMAs in one QK^T tile
+  constexpr int EPS = 32 / NQK;  // softmax elements per lane interleaved with each MFMA
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BLK * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BLK * VROW];
   __shared__ float sRed[2][NW];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave index as a wave-uniform (scalar) value, so per-wave quantities stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
 
   // ---- which (batch, head pack, query tile) this workgroup owns.
@@ -181,7 +206,7 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
   const int b = p / packs, hp = p % packs;
   const int t = a.nqt - 1 - trank;
   const int hq = hp * HPACK + (wave >> 1);
-  const int g = hq / a.group;
+  const int g = (hp * HPACK) / a.group;  // every head of the pack shares this KV head
   const int qi = t * BLK + (wave & 1) * 32 + l32;  // this lane's query row
 
   // ---- Q^T fragments (B operand of S^T = K Q^T): d = 16*ks + 8*half + [0, 8)
@@ -204,23 +229,38 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
   int e0 = ldc(a.row_ptr, t), e1 = ldc(a.row_ptr, t + 1);
   e0 = e0 < 0 ? 0 : (e0 > a.nnz ? (int)a.nnz : e0);
   e1 = e1 < e0 ? e0 : (e1 > a.nnz ? (int)a.nnz : e1);
+  const int nkb = a.nqt;  // key blocks = query tiles (square 64x64 tiles)
+  auto col_at = [&](int e) {
+    const int c = ldc(a.col, e);
+    return c < 0 ? 0 : (c > nkb ? nkb : c);
+  };
 
-  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)g * a.skh;
-  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)g * a.svh;
-  const int nmax = a.N - 1;
+  // Buffer views of this (batch, KV head)'s K and V rows: exactly N rows.
+  const uint32_t k_bytes = (uint32_t)(((int64_t)(a.N - 1) * a.skn + D) * 2);
+  const uint32_t v_bytes = (uint32_t)(((int64_t)(a.N - 1) * a.svn + D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + (int64_t)b * a.skb + (int64_t)g * a.skh), (short)0, (int)k_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v + (int64_t)b * a.svb + (int64_t)g * a.svh), (short)0, (int)v_bytes, 0x00020000);
+  const uint32_t k_tile_bytes = (uint32_t)(BLK * a.skn * 2);
+  const uint32_t v_tile_bytes = (uint32_t)(BLK * a.svn * 2);
+  using ST = Stage<D, NT>;
+  ST stk, stv;
+  stk.init(tid, a.skn);
+  stv.init(tid, a.svn);
 
-  // S^T = K(tile) Q^T for this wave's 32 queries: two 32x32 key tiles.
-  auto qk = [&](const uint16_t* tile, f32x16_t (&s)[2]) {
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            tile + (mt * 32 + l32) * KROW + ks * 16 + half * 8);
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
-      }
+  // LDS read bases: K operand rows (l32 [+32]) at d = 16*ks + 8*half; V^T transpose
+  // reads at row 4*half + jl/4, column 16*((lane/16)%2) + 4*(jl%4) of each 16-key step.
+  const int kbase_el = l32 * KROW + half * 8;
+  const int jl = lane & 15;
+  const int vbase_el = (4 * half + (jl >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
+
+  // One S^T MFMA step st of QK^T: key tile mt = st / KS, d-step ks = st % KS.
+  auto qk_step = [&](const uint16_t* tile, f32x16_t (&s)[2], int st) {
+    const int mt = st / KS, ks = st % KS;
+    const bf16x8_t kf =
+        *reinterpret_cast<const bf16x8_t*>(tile + kbase_el + mt * 32 * KROW + ks * 16);
+    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
   };
 
   // Mask a PARTIAL tile element-wise and return this lane's maximum (raw units).
@@ -242,22 +282,19 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
     return mx;
   };
 
-  // The gate: block maxima of every wave to LDS, one barrier, then per-head decisions.
-  auto gate = [&](float mx, int slot, int cls, bool& keep_h, bool& any_keep, float& tmax_h) {
-    const float wm = wave_max(mx);
-    if (lane == 0) sRed[slot][wave] = wm;
-    __syncthreads();
+  // Per-head keep decisions for the tile whose wave maxima sit in sRed[slot].
+  auto decide = [&](int slot, int cls, TileState& st) {
     const bool forced = (cls & BSFA_CLS_FORCED) != 0;
-    any_keep = false;
+    st.any = false;
 #pragma unroll
     for (int j = 0; j < HPACK; ++j) {
       const float tm = fmaxf(sRed[slot][2 * j], sRed[slot][2 * j + 1]) * a.scale;
       const bool kj = forced || (tm >= tau_pack[j]);
       if (j == (wave >> 1)) {
-        keep_h = kj;
-        tmax_h = tm;
+        st.keep = kj;
+        st.tmax = tm;
       }
-      any_keep = any_keep || kj;
+      st.any = st.any || kj;
     }
   };
 
@@ -267,136 +304,186 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
   unsigned n_kept = 0, n_skip = 0;
-
-  f32x16_t s_cur[2];
-  float mx_cur = -INFINITY, tmax_cur = 0.0f;
-  bool keep_cur = false, any_cur = false;
-
-  // Register staging: kr holds K(e+2) and vr holds V(e+1) while iteration e runs.
-  u32x4_t kr[ST::CPT], vr[ST::CPT];
-  if (e0 < e1) {
-    ST::load(kr, kbase, a.skn, ldc(a.col, e0), nmax, tid);
-    ST::template store<KROW>(sK[0], kr, tid);
-    if (e0 + 1 < e1) {
-      ST::load(kr, kbase, a.skn, ldc(a.col, e0 + 1), nmax, tid);
-      ST::template store<KROW>(sK[1], kr, tid);
-    }
-    __syncthreads();
-    qk(sK[0], s_cur);
-    mx_cur = mask_max(s_cur, ldc(a.col, e0), ldc_byte(a.cls, e0));
-    if constexpr (GATE) {
-      gate(mx_cur, 0, ldc_byte(a.cls, e0), keep_cur, any_cur, tmax_cur);
-    } else {
-      keep_cur = any_cur = true;
-    }
-    if (any_cur) {
-      ST::load(vr, vbase, a.svn, ldc(a.col, e0), nmax, tid);
-      ST::template store<VROW>(sV[0], vr, tid);
-    }
-    if (e0 + 2 < e1) ST::load(kr, kbase, a.skn, ldc(a.col, e0 + 2), nmax, tid);
-    if (!GATE && e0 + 1 < e1) ST::load(vr, vbase, a.svn, ldc(a.col, e0 + 1), nmax, tid);
-  }
-
   const float c2 = a.scale_log2;
-  for (int e = e0; e < e1; ++e) {
-    const int i = e - e0;
-    const bool has_next = e + 1 < e1;
-    __syncthreads();  // K(e+1) in sK[(i+1)&1], V(e) in sV[i&1]; iteration e-1 finished
 
-    // ---- softmax of tile e (kept tiles only): P in bf16, running max/sum update.
-    // The reference max is raised only when some row's max grows by more than 2^8 in
-    // exp2 units (or on a row's first keys), so P <= 256 and O rarely needs rescaling.
-    bf16x8_t pb[4];
-    bool rescale = false;
-    float alpha = 1.0f;
-    if (keep_cur) {
-      float x0, x1;
-      pair32(mx_cur, x0, x1);
-      const float m_new = fmaxf(m_run, fmaxf(x0, x1));
-      const bool grow = (m_run == -INFINITY) ? (m_new != -INFINITY)
-                                             : ((m_new - m_run) * c2 > 8.0f);
-      rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
-      if (rescale) {
-        alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-        m_run = m_new;
-        l_run *= alpha;
-      }
-      const float mb = (m_run == -INFINITY ? 0.0f : m_run) * c2;
-      float rs = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s_cur[ks >> 1][8 * (ks & 1) + j], c2, -mb));
-          rs += pv;
-          pb[ks][j] = (__bf16)pv;
-        }
-      l_run += rs;
+  u32x4_t kr[Stage<D, NT>::CPT], vr[Stage<D, NT>::CPT];
+  f32x16_t sA[2], sB[2];
+  TileState stA{-INFINITY, 0.0f, false, false}, stB{-INFINITY, 0.0f, false, false};
+
+  // Softmax bookkeeping for a kept tile: the reference max is raised only when some
+  // row's max grows by more than 2^8 in exp2 units (or on a row's first keys), so
+  // P <= 256 and O rarely needs rescaling. Returns the exp2 offset for the tile.
+  auto softmax_prep = [&](float mx, bool& rescale, float& alpha) -> float {
+    float x0, x1;
+    pair32(mx, x0, x1);
+    const float m_new = fmaxf(m_run, fmaxf(x0, x1));
+    const bool grow =
+        (m_run == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run) * c2 > 8.0f);
+    rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+    alpha = 1.0f;
+    if (rescale) {
+      alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      m_run = m_new;
+      l_run *= alpha;
     }
+    return (m_run == -INFINITY ? 0.0f : m_run) * c2;
+  };
 
-    // ---- scores and block maximum of tile e+1
-    f32x16_t s_nxt[2];
-    float mx_nxt = -INFINITY, tmax_nxt = 0.0f;
-    bool keep_nxt = true, any_nxt = true;
-    if (has_next) {
-      qk(sK[(i + 1) & 1], s_nxt);
-      mx_nxt = mask_max(s_nxt, ldc(a.col, e + 1), ldc_byte(a.cls, e + 1));
-      if constexpr (GATE) {
-        gate(mx_nxt, (i + 1) & 1, ldc_byte(a.cls, e + 1), keep_nxt, any_nxt, tmax_nxt);
-        if (any_nxt) ST::load(vr, vbase, a.svn, ldc(a.col, e + 1), nmax, tid);
+  // O^T += V(tile)^T P^T, after applying a pending rescale.
+  auto pv = [&](const uint16_t* vtile, const bf16x8_t (&pb)[4], bool rescale, float alpha) {
+    if (rescale) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const uint16_t* vt = vtile + vbase_el;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* p0 = vt + 16 * ks * VROW + 32 * dt;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(p0));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(p0 + 8 * VROW));
+        // Whole-vector concatenation and bit cast: an element-by-element copy from the
+        // two i16x4 results into a bf16x8 is lowered with a wrong v_perm_b32 (it
+        // duplicated element 0) by this compiler.
+        const i16x8_t cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, cat);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[dt], 0, 0, 0);
       }
+    }
+  };
+
+  auto count_export = [&](int e, const TileState& st) {
+    if (st.keep) ++n_kept; else ++n_skip;
+    if (EXPORT && (wave & 1) == 0 && lane == 0) {
+      const int64_t idx = ((int64_t)b * a.Hq + hq) * a.nnz + e;
+      a.tile_max[idx] = st.tmax;
+      a.keep[idx] = st.keep ? 1 : 0;
+    }
+  };
+
+  // One pipeline step for tile e (scores in sc, state cur) that also produces tile e+1
+  // (sn, nxt); e + 1 < e1. KEEP is cur.keep, so each variant is straight-line code.
+  auto step = [&](auto keep_tag, const int e, f32x16_t (&sc)[2], TileState& cur,
+                  f32x16_t (&sn)[2], TileState& nxt) {
+    constexpr bool KEEP = decltype(keep_tag)::value;
+    const int i = e - e0;
+    const uint16_t* kt_next = sK[(i + 1) & 1];
+    bool rescale = false;
+    float alpha = 1.0f, mb = 0.0f;
+    if constexpr (KEEP) mb = softmax_prep(cur.mx, rescale, alpha);
+
+    // ---- S(e+1) = K(e+1) Q^T, interleaved with P(e) = exp2(S(e) * c2 - mb) in bf16
+    bf16x8_t pb[4];
+    float rs = 0.0f;
+    sn[0] = f32x16_t{};
+    sn[1] = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < NQK; ++st) {
+      qk_step(kt_next, sn, st);
+      if constexpr (KEEP) {
+#pragma unroll
+        for (int u = 0; u < EPS; ++u) {
+          const int j = st * EPS + u;
+          const float pv_ = __builtin_amdgcn_exp2f(fmaf(sc[j >> 4][j & 15], c2, -mb));
+          rs += pv_;
+          pb[j >> 3][j & 7] = (__bf16)pv_;
+        }
+      }
+    }
+    if constexpr (KEEP) l_run += rs;
+
+    // ---- block maximum of tile e+1; stage V(e) and K(e+2) into LDS
+    const int c_n = col_at(e + 1);
+    const int cls_n = ldc_byte(a.cls, e + 1);
+    nxt.mx = mask_max(sn, c_n, cls_n);
+    if constexpr (GATE) {
+      const float wm = wave_max(nxt.mx);
+      if (lane == 0) sRed[(i + 1) & 1][wave] = wm;
+    }
+    if (KEEP || cur.any) ST::template store<VROW>(sV[i & 1], vr, tid);
+    if (e + 2 < e1) ST::template store<KROW>(sK[i & 1], kr, tid);
+    __syncthreads();  // V(e), K(e+2) and the maxima of tile e+1 are visible
+
+    // ---- gate(e+1)
+    if constexpr (GATE) {
+      decide((i + 1) & 1, cls_n, nxt);
+    } else {
+      nxt.keep = nxt.any = true;
     }
 
     // ---- O^T += V(e)^T P(e)^T
-    if (keep_cur) {
-      if (rescale) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      // V^T operand via ds_read_tr16_b64: lane (half h, in-group index jl) addresses
-      // row 16*ks + 4*h + jl/4 (+8 for the second read), column 32*dt + 16*((lane/16)%2)
-      // + 4*(jl%4); all (ks, dt) steps are immediate offsets from one base.
-      const int jl = lane & 15;
-      const uint16_t* vt = sV[i & 1] + (4 * half + (jl >> 2)) * VROW + 16 * ((lane >> 4) & 1) +
-                           4 * (jl & 3);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* p0 = vt + 16 * ks * VROW + 32 * dt;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(p0));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(p0 + 8 * VROW));
-          // Whole-vector concatenation and bit cast: an element-by-element copy from
-          // the two i16x4 results into a bf16x8 is lowered with a wrong v_perm_b32
-          // (it duplicated element 0) by this compiler.
-          const i16x8_t cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, cat);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[dt], 0, 0, 0);
-        }
-      }
+    if constexpr (KEEP) pv(sV[i & 1], pb, rescale, alpha);
+
+    // ---- loads of V(e+1) (only if some head keeps it) and K(e+3); they land while the
+    // next step's QK^T/softmax block runs, and are staged just before its barrier.
+    if (nxt.any) stv.load(vr, vrs, (uint32_t)c_n * v_tile_bytes);
+    if (e + 3 < e1) stk.load(kr, krs, (uint32_t)col_at(e + 3) * k_tile_bytes);
+    count_export(e, cur);
+  };
+
+  if (e0 < e1) {
+    // prologue: K(e0), K(e0+1) staged; S(e0) and its gate; loads of V(e0) and K(e0+2)
+    stk.load(kr, krs, (uint32_t)col_at(e0) * k_tile_bytes);
+    ST::template store<KROW>(sK[0], kr, tid);
+    if (e0 + 1 < e1) {
+      stk.load(kr, krs, (uint32_t)col_at(e0 + 1) * k_tile_bytes);
+      ST::template store<KROW>(sK[1], kr, tid);
     }
-    if (keep_cur) ++n_kept; else ++n_skip;
-    if (EXPORT && (wave & 1) == 0 && lane == 0) {
-      const int64_t idx = ((int64_t)b * a.Hq + hq) * a.nnz + e;
-      a.tile_max[idx] = tmax_cur;
-      a.keep[idx] = keep_cur ? 1 : 0;
+    __syncthreads();
+    sA[0] = f32x16_t{};
+    sA[1] = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < NQK; ++st) qk_step(sK[0], sA, st);
+    const int cls0 = ldc_byte(a.cls, e0);
+    stA.mx = mask_max(sA, col_at(e0), cls0);
+    if constexpr (GATE) {
+      const float wm = wave_max(stA.mx);
+      if (lane == 0) sRed[0][wave] = wm;
     }
-    // Stage K(e+2) and V(e+1) (loads issued one iteration / one P.V earlier); their
-    // buffers were last read in iteration e-1, and the next barrier publishes them.
-    if (e + 2 < e1) ST::template store<KROW>(sK[i & 1], kr, tid);
-    if (has_next && any_nxt) ST::template store<VROW>(sV[(i + 1) & 1], vr, tid);
-    if (e + 3 < e1) ST::load(kr, kbase, a.skn, ldc(a.col, e + 3), nmax, tid);
-    if (!GATE && e + 2 < e1) ST::load(vr, vbase, a.svn, ldc(a.col, e + 2), nmax, tid);
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
-    mx_cur = mx_nxt;
-    tmax_cur = tmax_nxt;
-    keep_cur = keep_nxt;
-    any_cur = any_nxt;
+    __syncthreads();  // maxima visible; every wave is done reading sK[0]
+    if constexpr (GATE) {
+      decide(0, cls0, stA);
+    } else {
+      stA.keep = stA.any = true;
+    }
+    if (stA.any) stv.load(vr, vrs, (uint32_t)col_at(e0) * v_tile_bytes);
+    if (e0 + 2 < e1) stk.load(kr, krs, (uint32_t)col_at(e0 + 2) * k_tile_bytes);
+
+    for (int e = e0; e + 1 < e1; ++e) {
+      if (stA.keep)
+        step(std::true_type{}, e, sA, stA, sB, stB);
+      else
+        step(std::false_type{}, e, sA, stA, sB, stB);
+      sA[0] = sB[0];
+      sA[1] = sB[1];
+      stA = stB;
+    }
+
+    // ---- the last tile: softmax, stage its V, P.V
+    const int e = e1 - 1, i = e - e0;
+    bf16x8_t pb[4];
+    bool rescale = false;
+    float alpha = 1.0f;
+    if (stA.keep) {
+      const float mb = softmax_prep(stA.mx, rescale, alpha);
+      float rs = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float pv_ = __builtin_amdgcn_exp2f(fmaf(sA[j >> 4][j & 15], c2, -mb));
+        rs += pv_;
+        pb[j >> 3][j & 7] = (__bf16)pv_;
+      }
+      l_run += rs;
+    }
+    if (stA.any) ST::template store<VROW>(sV[i & 1], vr, tid);
+    __syncthreads();
+    if (stA.keep) pv(sV[i & 1], pb, rescale, alpha);
+    count_export(e, stA);
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale * m + ln l; one store per element
