@@ -395,7 +395,13 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
         }
       }
     }
-    if constexpr (KEEP) l_run += rs;
+    if constexpr (KEEP) {
+      l_run += rs;
+      // Keep P(e) here, next to the QK^T MFMAs it overlaps with: without a use at this
+      // point the exp/convert work is sunk past the barrier into the P.V block.
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : : "v"(pb[ks]));
+    }
 
     // ---- block maximum of tile e+1; stage V(e) and K(e+2) into LDS
     const int c_n = col_at(e + 1);
