@@ -460,7 +460,19 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
     if (stA.any) stv.load(vr, vrs, (uint32_t)col_at(e0) * v_tile_bytes);
     if (e0 + 2 < e1) stk.load(kr, krs, (uint32_t)col_at(e0 + 2) * k_tile_bytes);
 
-    for (int e = e0; e + 1 < e1; ++e) {
+    // Unrolled by two so the scores alternate between sA and sB without copies.
+    int e = e0;
+    for (; e + 2 < e1; e += 2) {
+      if (stA.keep)
+        step(std::true_type{}, e, sA, stA, sB, stB);
+      else
+        step(std::false_type{}, e, sA, stA, sB, stB);
+      if (stB.keep)
+        step(std::true_type{}, e + 1, sB, stB, sA, stA);
+      else
+        step(std::false_type{}, e + 1, sB, stB, sA, stA);
+    }
+    if (e + 1 < e1) {
       if (stA.keep)
         step(std::true_type{}, e, sA, stA, sB, stB);
       else
@@ -468,10 +480,11 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
       sA[0] = sB[0];
       sA[1] = sB[1];
       stA = stB;
+      ++e;
     }
 
     // ---- the last tile: softmax, stage its V, P.V
-    const int e = e1 - 1, i = e - e0;
+    const int i = e - e0;
     bf16x8_t pb[4];
     bool rescale = false;
     float alpha = 1.0f;
