@@ -255,9 +255,9 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
   const int jl = lane & 15;
   const int vbase_el = (4 * half + (jl >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
 
-  // One S^T MFMA step st of QK^T: key tile mt = st / KS, d-step ks = st % KS.
+  // One S^T MFMA step st of QK^T: key tile mt = st % 2, d-step ks = st / 2.
   auto qk_step = [&](const uint16_t* tile, f32x16_t (&s)[2], int st) {
-    const int mt = st / KS, ks = st % KS;
+    const int mt = st & 1, ks = st >> 1;  // alternate the two accumulator chains
     const bf16x8_t kf =
         *reinterpret_cast<const bf16x8_t*>(tile + kbase_el + mt * 32 * KROW + ks * 16);
     s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
