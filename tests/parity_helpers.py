@@ -1,5 +1,10 @@
 """Shared plumbing for the GPU parity tests: run the HIP path and the CPU oracle on the
-same seeded inputs and compare them (keep mask, block maxima, O, LSE)."""
+same seeded inputs and compare them (keep mask, block maxima, O, LSE).
+
+The oracle runs on reduced fp64 arrays that hold only the compared query heads (each
+with its own copy of its KV head), so full-size workloads can be checked on sampled
+heads and query tiles.
+"""
 from __future__ import annotations
 
 import math
@@ -40,20 +45,37 @@ def gpu_spec(w: inputs.Workload):
     return bsfa.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
 
 
-def oracle_tau(w: inputs.Workload, quantile: float, q_tiles=None, seed: int = 1) -> np.ndarray:
-    """Per-head tau from the oracle's calibration on the calibration seed."""
-    qb, kb, _ = inputs.generate(w, seed)
-    return orc.calibrate_tau(f64(qb), f64(kb), oracle_spec(w), quantile, q_tiles=q_tiles)
+def reduced(w: inputs.Workload, qb, kb, vb, heads):
+    """fp64 [B, len(heads), N, d] arrays for the listed query heads, K/V per head."""
+    groups = [h // w.group for h in heads]
+    return f64(qb[:, heads]), f64(kb[:, groups]), f64(vb[:, groups])
 
 
-def dense_keep(lists, keep_sparse: np.ndarray, q_tiles) -> np.ndarray:
-    """Scatter the GPU's per-entry keep bits [B, Hq, nnz] to [B, Hq, len(q_tiles), nkb]."""
-    bsz, hq, _ = keep_sparse.shape
+def oracle_tau(w: inputs.Workload, quantile: float, q_tiles=None, heads=None,
+               seed: int = 1) -> np.ndarray:
+    """Per-head tau from the oracle's calibration on the calibration seed.
+
+    With ``heads`` given, only those heads are calibrated (their KV groups generated);
+    the other entries get the median of the calibrated ones (any value is a valid input:
+    those heads are not compared)."""
+    heads = list(range(w.Hq)) if heads is None else list(heads)
+    groups = sorted({h // w.group for h in heads})
+    qb, kb, _ = inputs.generate(w, seed, groups=groups)
+    q, k, _ = reduced(w, qb, kb, kb, heads)
+    taus = orc.calibrate_tau(q, k, oracle_spec(w), quantile, q_tiles=q_tiles)
+    out = np.full(w.Hq, float(np.median(taus)))
+    out[heads] = taus
+    return out
+
+
+def dense_grid(lists, per_entry: np.ndarray, q_tiles) -> np.ndarray:
+    """Scatter per-CSR-entry values [B, H, nnz] to [B, H, len(q_tiles), nkb]."""
+    bsz, nh, _ = per_entry.shape
     nkb = lists.n_qtiles
-    out = np.zeros((bsz, hq, len(q_tiles), nkb), dtype=keep_sparse.dtype)
+    out = np.zeros((bsz, nh, len(q_tiles), nkb), dtype=per_entry.dtype)
     for ti, t in enumerate(q_tiles):
         e0, e1 = lists.row_ptr_host[t], lists.row_ptr_host[t + 1]
-        out[:, :, ti, lists.col_host[e0:e1]] = keep_sparse[:, :, e0:e1]
+        out[:, :, ti, lists.col_host[e0:e1]] = per_entry[:, :, e0:e1]
     return out
 
 
@@ -75,18 +97,19 @@ def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
     nqt = -(-w.N // 64)
     q_tiles = list(range(nqt)) if q_tiles is None else list(q_tiles)
     heads = list(range(w.Hq)) if heads is None else list(heads)
-    q, k, v = f64(qb), f64(kb), f64(vb)
+    q, k, v = reduced(w, qb, kb, vb, heads)
+    tau_r = None if tau is None else np.asarray(tau, dtype=np.float64)[heads]
     near_cnt, tmax_err = 0, 0.0
     override = None
     kept = total = 0
     if tau is not None and res.keep is not None:
-        keep_gpu = res.keep.cpu().numpy().astype(bool)
-        tmax_gpu = res.tile_max.cpu().numpy().astype(np.float64)
-        kd = dense_keep(res.lists, keep_gpu, q_tiles)[:, heads]
-        md = dense_keep(res.lists, tmax_gpu, q_tiles)[:, heads]
-        ref = orc.attention(q, k, v, spec, tau=tau, q_tiles=q_tiles, heads=heads)
+        keep_gpu = res.keep[:, heads].cpu().numpy().astype(bool)
+        tmax_gpu = res.tile_max[:, heads].cpu().numpy().astype(np.float64)
+        kd = dense_grid(res.lists, keep_gpu, q_tiles)
+        md = dense_grid(res.lists, tmax_gpu, q_tiles)
+        ref = orc.attention(q, k, v, spec, tau=tau_r, q_tiles=q_tiles)
         allowed = ref.allowed[None, None]
-        tau_h = np.asarray(tau, dtype=np.float64)[heads][None, :, None, None]
+        tau_h = tau_r[None, :, None, None]
         near = (np.abs(ref.tile_max - tau_h) <= NEAR_TAU) & allowed & ~ref.forced[None, None]
         near_cnt = int(near.sum())
         if near_cnt:
@@ -100,17 +123,14 @@ def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
         override = kd
         kept = int((kd & allowed).sum())
         total = int(np.broadcast_to(allowed, kd.shape).sum())
-    ref = orc.attention(q, k, v, spec, tau=tau, q_tiles=q_tiles, heads=heads,
-                        keep_override=override)
-    out = res.out.float().cpu().numpy()
-    lse = res.lse.cpu().numpy()
+    ref = orc.attention(q, k, v, spec, tau=tau_r, q_tiles=q_tiles, keep_override=override)
     o_err, l_err = [], []
     for ti, t in enumerate(q_tiles):
         r0, r1 = t * 64, min(t * 64 + 64, w.N)
-        go = out[:, heads, r0:r1]
+        go = res.out[:, heads, r0:r1].float().cpu().numpy()
         ro = ref.out[:, :, ti, : r1 - r0]
         o_err.append(np.abs(go - ro).reshape(-1))
-        gl = lse[:, heads, r0:r1]
+        gl = res.lse[:, heads, r0:r1].cpu().numpy()
         rl = ref.lse[:, :, ti, : r1 - r0]
         both_inf = np.isneginf(gl) & np.isneginf(rl)
         l_err.append(np.where(both_inf, 0.0, np.abs(gl - rl)).reshape(-1))
@@ -118,8 +138,9 @@ def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
     l_err = np.concatenate(l_err)
     rep = Report(float(o_err.max()), float(o_err.mean()), float(l_err.max()), near_cnt,
                  kept, total, tmax_err)
-    log(f"{w.name} N={w.N} Hq={w.Hq}: max|dO|={rep.o_max:.3e} mean|dO|={rep.o_mean:.3e} "
-        f"max|dLSE|={rep.lse_max:.3e} max|dM|={rep.tmax_err:.2e} near={near_cnt}")
+    log(f"{w.name} N={w.N} Hq={w.Hq} heads={len(heads)} tiles={len(q_tiles)}: "
+        f"max|dO|={rep.o_max:.3e} mean|dO|={rep.o_mean:.3e} max|dLSE|={rep.lse_max:.3e} "
+        f"max|dM|={rep.tmax_err:.2e} near={near_cnt} kept={kept}/{total}")
     assert np.isfinite(o_err).all(), "non-finite output"
     assert rep.o_max <= O_MAX and rep.o_mean <= O_MEAN, rep
     assert rep.lse_max <= LSE_MAX, rep

@@ -110,3 +110,37 @@ def test_gqa_planted_16k_sampled():
     st = res.stats.cpu().numpy()[0]
     frac = st[:, 1].sum() / (st.sum() - w.Hq * nqt)
     ph.log(f"eligible skip fraction at the calibrated tau: {frac:.3f}")
+
+
+def _full_size(name, tiles_of, cal_of, dense_too=False):
+    w = W[name]
+    nqt = w.N // 64
+    heads = [g * w.group + g % w.group for g in range(w.Hkv)]  # one query head per KV head
+    tiles = tiles_of(nqt)
+    ph.log(f"case {name} (full size): B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}; "
+           f"oracle on heads {heads}, query tiles {tiles}")
+    tau = ph.oracle_tau(w, 0.5, q_tiles=cal_of(nqt), heads=heads)
+    qb, kb, vb = inputs.generate(w, 0)
+    res = ph.run_gpu(w, qb, kb, vb, tau)
+    ph.compare(w, qb, kb, vb, res, tau, q_tiles=tiles, heads=heads)
+    st = res.stats.cpu().numpy()
+    assert np.all(st.sum(-1) == res.lists.nnz)
+    eligible = res.lists.nnz - int(((res.lists.cls_host & 2) != 0).sum())
+    frac = st[0, heads, 1].sum() / (len(heads) * eligible)
+    ph.log(f"eligible skip fraction on the compared heads: {frac:.3f}")
+    if dense_too:
+        del res
+        res = ph.run_gpu(w, qb, kb, vb, None, export=False)
+        ph.compare(w, qb, kb, vb, res, None, q_tiles=tiles, heads=heads)
+
+
+def test_sink_local_64k_full_size_sampled():
+    """The benchmark workload at full size, gated and dense, in bench.py's launch shape."""
+    _full_size("sink_local_64k", lambda n: [0, 1, n // 2, n - 2, n - 1],
+               lambda n: [n // 4, n // 2, (3 * n) // 4], dense_too=True)
+
+
+def test_gqa70b_planted_128k_full_size_sampled():
+    """The 70B-shaped layer (Hq=64, Hkv=8, N=131072, causal + 128 global tokens)."""
+    _full_size("gqa70b_planted_128k", lambda n: [0, n // 2, n - 1],
+               lambda n: [n // 3, (2 * n) // 3])
