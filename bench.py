@@ -195,10 +195,24 @@ def main():
     lists = bsfa.BlockLists.get(mask, w.N, dev)
 
     quantiles = sorted(set([args.quantile] + (list(w.tau_quantiles) if args.sweep else [])))
-    taus = bsfa.calibrate_tau(qc_d, kc_d, mask, quantiles)
-    del qc_d, kc_d
+    taus = bsfa.calibrate_tau(qc_d, kc_d, mask, quantiles, lists=lists)
     torch.cuda.synchronize()
     log(f"[bench] calibrated tau for quantiles {quantiles}")
+    # the gate-only calibration pass on its own (tau = NaN: block maxima and their export)
+    nan_tau = torch.full((w.Hq,), math.nan, device=dev)
+    cal_ms = []
+    for it in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bsfa.fwd(qc_d, kc_d, kc_d, mask=mask, tau=nan_tau, want_lse=False,
+                 export_tiles=True, lists=lists)
+        e1.record()
+        torch.cuda.synchronize()
+        if it:
+            cal_ms.append(e0.elapsed_time(e1))
+    log(f"[bench] gate-only calibration pass: {np.mean(cal_ms):.3f} ms")
+    del qc_d, kc_d, nan_tau
+    torch.cuda.empty_cache()
 
     out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=out_dtype, device=dev)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
@@ -289,6 +303,7 @@ def main():
         "kernel_ms_mean": round(head["kernel_ms"], 4),
         "hbm_algorithmic_gbs": round(alg_bytes / (head["kernel_ms"] / 1e3) / 1e9, 1),
         "block_lists_host_ms": round(lists_host_s * 1e3, 2),
+        "calibration_pass_ms": round(float(np.mean(cal_ms)), 4),
         "executed_flop_per_step": head["exec_flop"],
         "dense_flop_per_step": dense_flop,
     }

@@ -7,7 +7,7 @@ it, which raises if the library is missing.
 """
 _BINDING_NAMES = {
     "MaskSpec", "BlockLists", "BsfaError", "build_block_lists", "fwd", "skip_stats",
-    "library_path", "load_library", "calibrate_tau",
+    "library_path", "load_library", "calibrate_tau", "calibration_maxima",
 }
 
 

@@ -257,24 +257,38 @@ def skip_stats(stats_tensor, stream=None):
     return kept, skipped
 
 
-def calibrate_tau(q, k, mask: MaskSpec, quantile, softmax_scale: float = 0.0):
-    """One-time per-head threshold calibration (Block Sparse Flash Attention, "The
-    paper's improvements": thresholds learned once per layer and head on a small data set).
+def calibration_maxima(q, k, mask: MaskSpec, softmax_scale: float = 0.0, lists=None,
+                       stream=None):
+    """Block maxima of every eligible (allowed, not forced) tile, per query head.
 
-    tau_h = the ``quantile`` of the eligible (allowed, not forced) block maxima of query
-    head h on calibration inputs q, k, measured with the gated kernel at tau = -inf
-    (nothing skipped) and its per-tile export. ``quantile`` may be a scalar (returns fp32
-    [Hq]) or a sequence (returns fp32 [len(quantile), Hq])."""
+    One gate-only pass of the kernel: tau = NaN keeps forced tiles only, so every other
+    tile costs its S = scale * Q K^T, its block maximum and the export, with no softmax,
+    P.V or V load. Returns a list of Hq fp32 arrays, each [B * eligible tiles] (the
+    per-head histogram input of the calibration in Block Sparse Flash Attention, "The
+    paper's improvements")."""
     import torch
 
     hq = q.shape[1]
-    res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), -math.inf, device=q.device),
-              softmax_scale=softmax_scale, want_lse=False, export_tiles=True)
-    tmax = res.tile_max.float().cpu().numpy()  # [B, Hq, nnz]
+    res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), math.nan, device=q.device),
+              softmax_scale=softmax_scale, want_lse=False, export_tiles=True, lists=lists,
+              stream=stream)
+    torch.cuda.synchronize(q.device)  # the launch may sit on a stream other than torch's
+    tmax = res.tile_max.cpu().numpy()  # [B, Hq, nnz]
     eligible = (res.lists.cls_host & BSFA_CLS_FORCED) == 0
+    return [tmax[:, h, :][:, eligible].reshape(-1) for h in range(hq)]
+
+
+def calibrate_tau(q, k, mask: MaskSpec, quantile, softmax_scale: float = 0.0, lists=None,
+                  stream=None):
+    """One-time per-head threshold calibration (Block Sparse Flash Attention, "The
+    paper's improvements": thresholds learned once per layer and head on a small data set).
+
+    tau_h = the ``quantile`` of the eligible block maxima of query head h on calibration
+    inputs q, k (``calibration_maxima``). ``quantile`` may be a scalar (returns fp32
+    [Hq]) or a sequence (returns fp32 [len(quantile), Hq])."""
+    maxima = calibration_maxima(q, k, mask, softmax_scale, lists=lists, stream=stream)
     qs = np.atleast_1d(np.asarray(quantile, dtype=np.float64))
-    taus = np.empty((qs.size, hq), dtype=np.float32)
-    for h in range(hq):
-        vals = tmax[:, h, :][:, eligible].reshape(-1)
-        taus[:, h] = np.quantile(vals, qs) if vals.size else -np.inf
+    taus = np.empty((qs.size, len(maxima)), dtype=np.float32)
+    for h, vals in enumerate(maxima):
+        taus[:, h] = np.quantile(vals.astype(np.float64), qs) if vals.size else -np.inf
     return taus[0] if np.ndim(quantile) == 0 else taus

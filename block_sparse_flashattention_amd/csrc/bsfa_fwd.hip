@@ -92,13 +92,24 @@ __device__ __forceinline__ int ldc_byte(const uint8_t* p, int64_t i) {
   return (int)((w >> (8 * (i & 3))) & 0xFFu);
 }
 
-__device__ __forceinline__ bool allowed(int i, int j, int n, int causal, int window, int ng) {
-  // branch-free: bitwise combination of the static primitives
-  const int dist = i > j ? i - j : j - i;
-  const bool inside = (i < n) & (j < n);
-  const bool causal_ok = (causal == 0) | (j <= i);
-  const bool pattern = (window <= 0) | (dist < window) | (j < ng) | (i < ng);
-  return inside & causal_ok & pattern;
+// Bits [0, n) of a 64-bit word, n clamped to [0, 64].
+__device__ __forceinline__ uint64_t bits_below(int n) {
+  n = n < 0 ? 0 : (n > 64 ? 64 : n);
+  return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+}
+
+// Keys j0 + k, k in [0, 64), that query row i may attend, as bit k of the result: the
+// static primitives (causal, window, global tokens, j < N) as ranges of k.
+__device__ __forceinline__ uint64_t row_mask(int i, int j0, int n, int causal, int window,
+                                             int ng) {
+  const int r = i - j0;  // k of the diagonal element
+  uint64_t m = bits_below(n - j0);
+  if (causal) m &= bits_below(r + 1);
+  if (window > 0) {
+    const uint64_t w = bits_below(r + window) & ~bits_below(r - window + 1);
+    m &= (i < ng) ? ~0ull : (w | bits_below(ng - j0));
+  }
+  return i < n ? m : 0ull;
 }
 
 // LDS tiles are 64 rows x D bf16 with padded rows. K rows are D + 8 elements apart, so
@@ -255,24 +266,33 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
   const int jl = lane & 15;
   const int vbase_el = (4 * half + (jl >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
 
-  // One S^T MFMA step st of QK^T: key tile mt = st % 2, d-step ks = st / 2.
+  // K fragment (A operand) of S^T MFMA step st: key tile mt = st % 2, d-step ks = st / 2.
+  auto k_frag = [&](const uint16_t* tile, int st) {
+    const int mt = st & 1, ks = st >> 1;
+    return *reinterpret_cast<const bf16x8_t*>(tile + kbase_el + mt * 32 * KROW + ks * 16);
+  };
+  // One S^T MFMA step st of QK^T (the two accumulator chains alternate).
   auto qk_step = [&](const uint16_t* tile, f32x16_t (&s)[2], int st) {
-    const int mt = st & 1, ks = st >> 1;  // alternate the two accumulator chains
-    const bf16x8_t kf =
-        *reinterpret_cast<const bf16x8_t*>(tile + kbase_el + mt * 32 * KROW + ks * 16);
-    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
+    s[st & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(tile, st), qf[st >> 1],
+                                                        s[st & 1], 0, 0, 0);
   };
 
   // Mask a PARTIAL tile element-wise and return this lane's maximum (raw units).
   auto mask_max = [&](f32x16_t (&s)[2], int c, int cls) -> float {
     if (cls & BSFA_CLS_PARTIAL) {
+      // Element i of chain mt holds key mt*32 + 8*(i/4) + 4*half + i%4 of the block.
+      const uint64_t m = row_mask(qi, c * BLK, a.N, a.causal, a.window, a.n_global);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint32_t w = (uint32_t)(m >> (32 * mt)) >> (4 * half);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int j = c * BLK + mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (!allowed(qi, j, a.N, a.causal, a.window, a.n_global)) s[mt][i] = -INFINITY;
+          // A select, not an and/or blend of the bits: this compiler lowers the blend to
+          // v_bitop3_b32 forms that gave wrong elements.
+          const uint32_t bit = __builtin_amdgcn_ubfe(w, 8 * (i >> 2) + (i & 3), 1);
+          s[mt][i] = bit ? s[mt][i] : -INFINITY;
         }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -382,10 +402,10 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
     float rs = 0.0f;
     sn[0] = f32x16_t{};
     sn[1] = f32x16_t{};
+    if constexpr (KEEP) {
 #pragma unroll
-    for (int st = 0; st < NQK; ++st) {
-      qk_step(kt_next, sn, st);
-      if constexpr (KEEP) {
+      for (int st = 0; st < NQK; ++st) {
+        qk_step(kt_next, sn, st);
 #pragma unroll
         for (int u = 0; u < EPS; ++u) {
           const int j = st * EPS + u;
@@ -393,6 +413,21 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
           rs += pv_;
           pb[j >> 3][j & 7] = (__bf16)pv_;
         }
+      }
+    } else {
+      // Skipped tile e: the registers of S(e) and P(e) are free, so the K fragments are
+      // read SPF MFMAs ahead and the MFMAs issue without waiting on LDS.
+      constexpr int SPF = NQK < 8 ? NQK : 8;
+      bf16x8_t kf[SPF];
+#pragma unroll
+      for (int st = 0; st < SPF; ++st) kf[st] = k_frag(kt_next, st);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+      for (int st = 0; st < NQK; ++st) {
+        const bf16x8_t kcur = kf[st % SPF];
+        if (st + SPF < NQK) kf[st % SPF] = k_frag(kt_next, st + SPF);
+        sn[st & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[st >> 1], sn[st & 1],
+                                                             0, 0, 0);
       }
     }
     if constexpr (KEEP) {
@@ -415,6 +450,10 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
     if (e + 2 < e1) ST::template store<KROW>(sK[i & 1], kr, tid);
     __syncthreads();  // V(e), K(e+2) and the maxima of tile e+1 are visible
 
+    // ---- loads of K(e+3) right away (its registers were just staged), so they have
+    // the rest of this step and the next QK^T block to land even when tiles are skipped
+    if (e + 3 < e1) stk.load(kr, krs, (uint32_t)col_at(e + 3) * k_tile_bytes);
+
     // ---- gate(e+1)
     if constexpr (GATE) {
       decide((i + 1) & 1, cls_n, nxt);
@@ -425,10 +464,8 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
     // ---- O^T += V(e)^T P(e)^T
     if constexpr (KEEP) pv(sV[i & 1], pb, rescale, alpha);
 
-    // ---- loads of V(e+1) (only if some head keeps it) and K(e+3); they land while the
-    // next step's QK^T/softmax block runs, and are staged just before its barrier.
+    // ---- loads of V(e+1), only if some head keeps it; staged before the next barrier
     if (nxt.any) stv.load(vr, vrs, (uint32_t)c_n * v_tile_bytes);
-    if (e + 3 < e1) stk.load(kr, krs, (uint32_t)col_at(e + 3) * k_tile_bytes);
     count_export(e, cur);
   };
 
