@@ -46,29 +46,27 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 64;
 
-__device__ __forceinline__ float dpp_max(float x, int ctrl_sel) {
-  // all lanes valid for the row/quad permutations used here
-  int y;
-  switch (ctrl_sel) {
-    case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad [1,0,3,2]
-    case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad [2,3,0,1]
-    case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false); break;  // row_ror:4
-    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false); break; // row_ror:8
-  }
-  return fmaxf(x, __int_as_float(y));
+// Order-preserving map of a float onto a signed int (for non-NaN values, -inf included),
+// so maxima can be reduced with integer max, which needs no NaN canonicalisation.
+__device__ __forceinline__ int f2ord(float x) {
+  const int b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float ord2f(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
 }
 
-// Maximum over the 64 lanes of a wave, returned as a wave-uniform value.
+// Maximum over the 64 lanes of a wave, returned as a wave-uniform value: halves swapped
+// across lane 32, then a DPP all-reduce inside each 16-lane row, then rows 0 and 1.
 __device__ __forceinline__ float wave_max(float x) {
-  x = dpp_max(x, 0);
-  x = dpp_max(x, 1);
-  x = dpp_max(x, 2);
-  x = dpp_max(x, 3);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  int k = f2ord(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+  k = max((int)sw[0], (int)sw[1]);
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x124, 0xF, 0xF, false));  // row_ror:4
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x128, 0xF, 0xF, false));  // row_ror:8
+  return ord2f(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)));
 }
 
 // {x[l], x[l ^ 32]} in some order, for every lane l.

@@ -58,7 +58,14 @@ bool all_allowed(const bsfa_mask_spec& m, int64_t r0, int64_t r1, int64_t c0, in
 }
 
 bool valid_strides(const bsfa_strides* s) {
-  return s && s->b % 8 == 0 && s->h % 8 == 0 && s->n % 8 == 0;
+  return s && s->b % 8 == 0 && s->h % 8 == 0 && s->n % 8 == 0 && s->b >= 0 && s->h >= 0 &&
+         s->n >= 0;
+}
+
+// K and V rows of one (batch, KV head) are read through a buffer view with a 32-bit
+// byte range: the view must span less than 2^31 bytes.
+bool view_fits(const bsfa_strides* s, int32_t N, int32_t d) {
+  return ((int64_t)(N - 1) * s->n + d) * 2 <= (int64_t)INT32_MAX;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -155,7 +162,9 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     return fail(BSFA_ERR_UNSUPPORTED, "block list arrays must be 4-byte aligned");
   if (!sq || !sk || !sv || !so) return fail(BSFA_ERR_INVALID_ARG, "strides are required");
   if (!valid_strides(sq) || !valid_strides(sk) || !valid_strides(sv) || !valid_strides(so))
-    return fail(BSFA_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+    return fail(BSFA_ERR_UNSUPPORTED, "strides must be non-negative multiples of 8 elements");
+  if (!view_fits(sk, N, d) || !view_fits(sv, N, d))
+    return fail(BSFA_ERR_UNSUPPORTED, "the K or V rows of one head span 2^31 bytes or more");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(BSFA_ERR_UNSUPPORTED, "q, k, v, out must be 16-byte aligned");
 

@@ -133,7 +133,9 @@ int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_
  *             block maximum M_tc and the keep decision; both NULL or both set; needs
  *             tau != NULL.
  *   stream  : hipStream_t (NULL = default stream). The call is asynchronous.
- * Pointers q, k, v, out must be 16-byte aligned and the n/h/b strides multiples of 8.
+ * Pointers q, k, v, out must be 16-byte aligned and the n/h/b strides non-negative
+ * multiples of 8. The K (and V) rows of one (batch, KV head), ((N - 1) * n-stride + d)
+ * elements, must span fewer than 2^31 bytes; otherwise BSFA_ERR_UNSUPPORTED.
  */
 int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,

@@ -64,9 +64,11 @@ def _fwd_call(lib, **kw):
                 mask=binding._CMask(1, 0, 0, 1, 1),
                 lists=binding._CLists(2, 64, 64, 3, 16, 16, 16),
                 tau=None, scale=0.0, out_dtype=0, stats=None, tile_max=None, keep=None)
+    skn = kw.pop("skn", 128)
+    sqn = kw.pop("sqn", 128)
     args.update(kw)
-    s = binding._CStrides(4 * 128 * 128, 128 * 128, 128)
-    sk = binding._CStrides(2 * 128 * 128, 128 * 128, 128)
+    s = binding._CStrides(4 * 128 * 128, 128 * 128, sqn)
+    sk = binding._CStrides(2 * 128 * 128, 128 * 128, skn)
     return lib.bsfa_fwd(args["q"], args["k"], args["v"], args["out"], args["lse"], args["B"],
                         args["Hq"], args["Hkv"], args["N"], args["d"], ctypes.byref(s),
                         ctypes.byref(sk), ctypes.byref(sk), ctypes.byref(s),
@@ -90,6 +92,8 @@ def _fwd_call(lib, **kw):
     (dict(q=None), -1),
     (dict(q=24), -2),                         # misaligned pointer
     (dict(B=-1), -1),
+    (dict(sqn=-128), -2),                     # negative stride
+    (dict(skn=1 << 24), -2),                  # one head's K/V rows span more than 2^31 bytes
 ])
 def test_fwd_argument_errors(kw, code):
     lib = bsfa.load_library()
