@@ -33,7 +33,9 @@ class BsfaError(RuntimeError):
 class _CMask(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("n_global", ctypes.c_int32), ("force_keep_diag", ctypes.c_int32),
-                ("force_keep_global", ctypes.c_int32)]
+                ("force_keep_global", ctypes.c_int32), ("dilation", ctypes.c_int32),
+                ("dilation_taps", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("random_ppm", ctypes.c_int32), ("random_seed", ctypes.c_int32)]
 
 
 class _CStrides(ctypes.Structure):
@@ -94,17 +96,25 @@ def _check(lib, status: int):
 
 @dataclass(frozen=True)
 class MaskSpec:
-    """Static pattern: causal AND (window OR global tokens); see include/bsfa.h."""
+    """Static pattern: causal AND the OR of the set primitives (window, dilated,
+    blockwise, random blocks, global tokens); see include/bsfa.h."""
 
     causal: bool = True
     window: int = 0
     n_global: int = 0
     force_keep_diag: bool = True
     force_keep_global: bool = True
+    dilation: int = 0
+    dilation_taps: int = 0
+    block: int = 0
+    random_ppm: int = 0
+    random_seed: int = 0
 
     def _c(self) -> _CMask:
         return _CMask(int(self.causal), int(self.window), int(self.n_global),
-                      int(self.force_keep_diag), int(self.force_keep_global))
+                      int(self.force_keep_diag), int(self.force_keep_global),
+                      int(self.dilation), int(self.dilation_taps), int(self.block),
+                      int(self.random_ppm), int(self.random_seed))
 
 
 def build_block_lists(mask: MaskSpec, n: int, block_q: int = 64, block_k: int = 64):

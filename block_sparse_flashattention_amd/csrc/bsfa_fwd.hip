@@ -27,6 +27,7 @@
 // keep/skip branch is uniform across the workgroup.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -91,23 +92,64 @@ __device__ __forceinline__ int ldc_byte(const uint8_t* p, int64_t i) {
 }
 
 // Bits [0, n) of a 64-bit word, n clamped to [0, 64].
-__device__ __forceinline__ uint64_t bits_below(int n) {
+__device__ __forceinline__ uint64_t bits_below(int64_t n) {
   n = n < 0 ? 0 : (n > 64 ? 64 : n);
   return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
 }
 
-// Keys j0 + k, k in [0, 64), that query row i may attend, as bit k of the result: the
-// static primitives (causal, window, global tokens, j < N) as ranges of k.
-__device__ __forceinline__ uint64_t row_mask(int i, int j0, int n, int causal, int window,
-                                             int ng) {
-  const int r = i - j0;  // k of the diagonal element
-  uint64_t m = bits_below(n - j0);
-  if (causal) m &= bits_below(r + 1);
-  if (window > 0) {
-    const uint64_t w = bits_below(r + window) & ~bits_below(r - window + 1);
-    m &= (i < ng) ? ~0ull : (w | bits_below(ng - j0));
+// Keys j0 + k, k in [0, 64), that query row i may attend, as bit k of the result: each
+// static primitive (causal, N, window, dilated, blockwise, global tokens) is a range or
+// a residue class of k; `rnd` says the random primitive selects this 64 x 64 tile.
+// The fields of the further primitives, read when a partial tile needs them. They are
+// loaded from the kernel argument segment through an address the compiler cannot track,
+// so the loads stay on this rare path instead of holding scalar registers for the whole
+// kernel (the gated kernel has none to spare).
+struct PatternArgs {
+  int32_t pattern, dilation, block, dil_span;
+  unsigned long long dil_bits;
+};
+__device__ __forceinline__ PatternArgs pattern_args() {
+  auto base = (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(base));
+  auto f = [&](size_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(base + off);
+  };
+  PatternArgs p;
+  p.pattern = f(offsetof(FwdArgs, pattern));
+  p.dilation = f(offsetof(FwdArgs, dilation));
+  p.block = f(offsetof(FwdArgs, block));
+  p.dil_span = f(offsetof(FwdArgs, dil_span));
+  p.dil_bits = *reinterpret_cast<const __attribute__((address_space(4))) unsigned long long*>(
+      base + offsetof(FwdArgs, dil_bits));
+  return p;
+}
+
+__device__ __forceinline__ uint64_t row_mask(const FwdArgs& a, int i, int j0, bool rnd) {
+  const PatternArgs pa = pattern_args();
+  const int r = i - j0;  // k of the diagonal element (|r| < N < 2^31)
+  uint64_t m = bits_below((int64_t)a.N - j0);
+  if (a.causal) m &= bits_below((int64_t)r + 1);
+  if (pa.pattern) {
+    uint64_t p = (i < a.n_global) ? ~0ull : bits_below((int64_t)a.n_global - j0);
+    if (a.window > 0)
+      p |= bits_below((int64_t)r + a.window) & ~bits_below((int64_t)r - a.window + 1);
+    if (pa.dilation > 0) {
+      const int st = pa.dilation;
+      const int off = ((r % st) + st) % st;  // keys k = off, off + st, ... below 64
+      uint64_t dm = 0;
+      if (off < 64) dm = (st >= 64 ? 1ull : pa.dil_bits) << off;
+      if (pa.dil_span > 0)
+        dm &= bits_below((int64_t)r + pa.dil_span) & ~bits_below((int64_t)r - pa.dil_span + 1);
+      p |= dm;
+    }
+    if (pa.block > 0) {
+      const int64_t lo = (int64_t)(i / pa.block) * pa.block;
+      p |= bits_below(lo + pa.block - j0) & ~bits_below(lo - j0);
+    }
+    if (rnd) p = ~0ull;
+    m &= p;
   }
-  return i < n ? m : 0ull;
+  return i < a.N ? m : 0ull;
 }
 
 // LDS tiles are 64 rows x D bf16 with padded rows. K rows are D + 8 elements apart, so
@@ -279,7 +321,7 @@ __global__ __launch_bounds__(128 * HPACK) void bsfa_fwd_kernel(const FwdArgs a) 
   auto mask_max = [&](f32x16_t (&s)[2], int c, int cls) -> float {
     if (cls & BSFA_CLS_PARTIAL) {
       // Element i of chain mt holds key mt*32 + 8*(i/4) + 4*half + i%4 of the block.
-      const uint64_t m = row_mask(qi, c * BLK, a.N, a.causal, a.window, a.n_global);
+      const uint64_t m = row_mask(a, qi, c * BLK, (cls & BSFA_CLS_RANDOM) != 0);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const uint32_t w = (uint32_t)(m >> (32 * mt)) >> (4 * half);

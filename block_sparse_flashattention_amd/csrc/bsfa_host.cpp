@@ -1,9 +1,11 @@
 // Host side of libbsfa: static block lists, argument validation, variant dispatch.
 //
-// Block classification is analytic per tile (no per-element loop): the static mask is
-// causal AND (window band OR global key OR global query), so "some element allowed"
-// and "every element allowed" reduce to interval tests on the tile's row and column
-// ranges.
+// Block classification. With only the causal, window and global primitives it is
+// analytic per tile: "some element allowed" and "every element allowed" reduce to
+// interval tests on the tile's row and column ranges. With the dilated, blockwise or
+// random primitives, a conservative per-primitive test first discards tiles no
+// primitive can reach; the remaining tiles are classified exactly from per-row 64-bit
+// masks of their allowed keys.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -57,6 +59,130 @@ bool all_allowed(const bsfa_mask_spec& m, int64_t r0, int64_t r1, int64_t c0, in
   return std::max(r1 - cc0, c1 - rr0) < m.window;
 }
 
+bool extra_primitives(const bsfa_mask_spec& m) {
+  return m.dilation > 0 || m.block > 0 || m.random_ppm > 0;
+}
+bool has_pattern(const bsfa_mask_spec& m) { return m.window > 0 || extra_primitives(m); }
+
+int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// SplitMix64 output for counter x (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014).
+uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// The random primitive's choice for 64-token query block t and key block c.
+bool random_block(const bsfa_mask_spec& m, int64_t t, int64_t c) {
+  if (m.random_ppm <= 0) return false;
+  const uint64_t counter = ((uint64_t)((uint32_t)m.random_seed & 0xFFFFFFu) << 40) |
+                           ((uint64_t)(t & 0xFFFFF) << 20) | (uint64_t)(c & 0xFFFFF);
+  const uint64_t threshold = ((uint64_t)m.random_ppm << 32) / 1000000u;
+  return (splitmix64(counter) >> 32) < threshold;
+}
+
+// Bits [0, n) of a 64-bit word, n clamped to [0, 64].
+uint64_t bits_below(int64_t n) {
+  if (n <= 0) return 0;
+  if (n >= 64) return ~0ull;
+  return (1ull << n) - 1ull;
+}
+
+// Bits at 0, s, 2s, ... below 64 (the dilated primitive's pattern for one residue).
+uint64_t stride_pattern(int32_t s) {
+  if (s <= 0) return 0;
+  uint64_t p = 0;
+  for (int k = 0; k < 64; k += s) p |= 1ull << k;
+  return p;
+}
+
+// Keys j0 + k (k in [0, 64)) that query row i may attend, as bit k.
+uint64_t row_bits(const bsfa_mask_spec& m, int64_t i, int64_t j0, int64_t N,
+                  uint64_t spat) {
+  if (i < 0 || i >= N) return 0;
+  const int64_t r = i - j0;  // k of the diagonal element
+  uint64_t mm = bits_below(N - j0);
+  if (m.causal) mm &= bits_below(r + 1);
+  if (!has_pattern(m)) return mm;
+  uint64_t p = (i < m.n_global) ? ~0ull : bits_below((int64_t)m.n_global - j0);
+  if (m.window > 0) p |= bits_below(r + m.window) & ~bits_below(r - m.window + 1);
+  if (m.dilation > 0) {
+    const int64_t st = m.dilation;
+    const int64_t off = ((r % st) + st) % st;
+    uint64_t dm = 0;
+    if (off < 64) dm = (st >= 64 ? 1ull : spat) << off;
+    if (m.dilation_taps > 0) {
+      const int64_t span = st * (int64_t)m.dilation_taps;
+      dm &= bits_below(r + span) & ~bits_below(r - span + 1);
+    }
+    p |= dm;
+  }
+  if (m.block > 0) {
+    const int64_t lo = (i / m.block) * (int64_t)m.block;
+    p |= bits_below(lo + m.block - j0) & ~bits_below(lo - j0);
+  }
+  if (m.random_ppm > 0) {  // the 64 keys may straddle two 64-token blocks
+    const int64_t cb = floor_div(j0, 64), split = (cb + 1) * 64 - j0;
+    const uint64_t low = bits_below(split);
+    if (random_block(m, i / 64, cb)) p |= low;
+    if (split < 64 && random_block(m, i / 64, cb + 1)) p |= ~low;
+  }
+  return mm & p;
+}
+
+// Can any primitive reach rows [r0, r1] x columns [c0, c1]? (May say yes wrongly,
+// never no wrongly.)
+bool may_hit(const bsfa_mask_spec& m, int64_t r0, int64_t r1, int64_t c0, int64_t c1) {
+  if (m.causal && c0 > r1) return false;
+  if (!has_pattern(m)) return true;
+  if (c0 < m.n_global || r0 < m.n_global) return true;
+  const int64_t dlo = m.causal ? std::max<int64_t>(r0 - c1, 0) : r0 - c1, dhi = r1 - c0;
+  if (m.window > 0 && std::max<int64_t>(dlo, -(int64_t)m.window + 1) <=
+                          std::min<int64_t>(dhi, m.window - 1))
+    return true;
+  if (m.dilation > 0) {
+    int64_t lo = dlo, hi = dhi;
+    if (m.dilation_taps > 0) {
+      const int64_t span = (int64_t)m.dilation * m.dilation_taps;
+      lo = std::max(lo, -span + 1);
+      hi = std::min(hi, span - 1);
+    }
+    if (lo <= hi && floor_div(hi, m.dilation) * m.dilation >= lo) return true;
+  }
+  if (m.block > 0 && std::max(r0 / m.block, c0 / m.block) <= std::min(r1 / m.block, c1 / m.block))
+    return true;
+  if (m.random_ppm > 0)
+    for (int64_t t = r0 / 64; t <= r1 / 64; ++t)
+      for (int64_t c = c0 / 64; c <= c1 / 64; ++c)
+        if (random_block(m, t, c)) return true;
+  return false;
+}
+
+// Exact "some element allowed" and "every element slot allowed" of a tile from its rows'
+// key masks. Slots past N count as not allowed.
+void classify_rows(const bsfa_mask_spec& m, int64_t r0, int64_t r1, int64_t c0, int64_t c1,
+                   int64_t bq, int64_t bk, int64_t N, uint64_t spat, bool& any, bool& all) {
+  any = false;
+  all = (r1 - r0 + 1 == bq) && (c1 - c0 + 1 == bk);
+  for (int64_t i = r0; i <= r1; ++i) {
+    for (int64_t j0 = c0; j0 <= c1; j0 += 64) {
+      const uint64_t width = bits_below(std::min<int64_t>(64, c1 - j0 + 1));
+      const uint64_t mm = row_bits(m, i, j0, N, spat) & width;
+      any = any || mm != 0;
+      all = all && mm == width;
+      if (any && !all) return;
+    }
+  }
+}
+
+bool valid_mask(const bsfa_mask_spec* m) {
+  return m->window >= 0 && m->n_global >= 0 && m->dilation >= 0 && m->dilation_taps >= 0 &&
+         m->block >= 0 && m->random_ppm >= 0 && m->random_ppm <= 1000000;
+}
+
 bool valid_strides(const bsfa_strides* s) {
   return s && s->b % 8 == 0 && s->h % 8 == 0 && s->n % 8 == 0 && s->b >= 0 && s->h >= 0 &&
          s->n >= 0;
@@ -76,7 +202,7 @@ extern "C" {
 
 const char* bsfa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t bsfa_abi_version(void) { return 1; }
+int32_t bsfa_abi_version(void) { return 2; }
 
 int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_q,
                            int32_t block_k, int32_t* row_ptr, int32_t* col, uint8_t* cls,
@@ -85,29 +211,42 @@ int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_
   if (N < 0 || block_q < 1 || block_k < 1)
     return fail(BSFA_ERR_INVALID_ARG, "need N >= 0 and block sizes >= 1 (N=%d bq=%d bk=%d)",
                 N, block_q, block_k);
-  if (mask->window < 0 || mask->n_global < 0)
-    return fail(BSFA_ERR_INVALID_ARG, "window and n_global must be >= 0");
+  if (!valid_mask(mask))
+    return fail(BSFA_ERR_INVALID_ARG,
+                "mask fields must be >= 0 and random_ppm at most 1000000");
   if (col && !cls) return fail(BSFA_ERR_INVALID_ARG, "col and cls must both be given");
   const int64_t nqt = ((int64_t)N + block_q - 1) / block_q;
   const int64_t nkb = ((int64_t)N + block_k - 1) / block_k;
   int64_t nnz = 0;
   bool overflow = false;
   if (row_ptr) row_ptr[0] = 0;
+  const bool general = extra_primitives(*mask);
+  const uint64_t spat = stride_pattern(mask->dilation);
   for (int64_t t = 0; t < nqt; ++t) {
     const int64_t r0 = t * block_q, r1 = std::min<int64_t>(r0 + block_q, N) - 1;
     const bool rows_whole = r0 + block_q <= N;
     for (int64_t c = 0; c < nkb; ++c) {
       const int64_t c0 = c * block_k, c1 = std::min<int64_t>(c0 + block_k, N) - 1;
-      if (!any_allowed(*mask, r0, r1, c0, c1)) continue;
+      bool any, all;
+      if (general) {
+        if (!may_hit(*mask, r0, r1, c0, c1)) continue;
+        classify_rows(*mask, r0, r1, c0, c1, block_q, block_k, N, spat, any, all);
+        if (!any) continue;
+      } else {
+        if (!any_allowed(*mask, r0, r1, c0, c1)) continue;
+        any = true;
+        all = rows_whole && c0 + block_k <= N && all_allowed(*mask, r0, r1, c0, c1);
+      }
       if (col) {
         if (nnz < capacity) {
-          const bool whole = rows_whole && c0 + block_k <= N;
           uint8_t k = 0;
-          if (!(whole && all_allowed(*mask, r0, r1, c0, c1))) k |= BSFA_CLS_PARTIAL;
+          if (!all) k |= BSFA_CLS_PARTIAL;
           const bool diag = std::max(r0, c0) <= std::min(r1, c1);
           const bool glob = c0 < std::min<int64_t>(mask->n_global, N);
           if ((mask->force_keep_diag && diag) || (mask->force_keep_global && glob))
             k |= BSFA_CLS_FORCED;
+          if (mask->random_ppm > 0 && random_block(*mask, r0 / 64, c0 / 64))
+            k |= BSFA_CLS_RANDOM;
           col[nnz] = (int32_t)c;
           cls[nnz] = k;
         } else {
@@ -138,6 +277,9 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     return fail(BSFA_ERR_INVALID_ARG, "need B >= 0, N >= 0, Hq >= 1, Hkv >= 1");
   if (Hq % Hkv != 0) return fail(BSFA_ERR_INVALID_ARG, "Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
   if (!mask || !lists) return fail(BSFA_ERR_INVALID_ARG, "mask and lists are required");
+  if (!valid_mask(mask))
+    return fail(BSFA_ERR_INVALID_ARG,
+                "mask fields must be >= 0 and random_ppm at most 1000000");
   if (out_dtype != BSFA_OUT_BF16 && out_dtype != BSFA_OUT_F32)
     return fail(BSFA_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
   if (!(softmax_scale >= 0.0f) || isinf(softmax_scale))
@@ -190,6 +332,14 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   a.causal = mask->causal != 0;
   a.window = mask->window;
   a.n_global = mask->n_global;
+  a.pattern = has_pattern(*mask) ? 1 : 0;
+  a.dilation = mask->dilation;
+  a.dil_span = mask->dilation_taps > 0
+                   ? (int32_t)std::min<int64_t>((int64_t)mask->dilation * mask->dilation_taps,
+                                                INT32_MAX)
+                   : 0;
+  a.block = mask->block;
+  a.dil_bits = stride_pattern(mask->dilation);
   a.row_ptr = lists->row_ptr;
   a.col = lists->col;
   a.cls = lists->cls;

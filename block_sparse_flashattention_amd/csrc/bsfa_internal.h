@@ -21,6 +21,10 @@ struct FwdArgs {
   int32_t nqt;    // ceil(N / 64)
   int32_t group;  // Hq / Hkv
   int32_t causal, window, n_global;
+  int32_t pattern;             // some pattern primitive is set (else all pairs pass)
+  int32_t dilation, block;
+  int32_t dil_span;             // dilation * taps clamped to 2^31 - 1; 0 = no limit
+  unsigned long long dil_bits;  // bits 0, s, 2s, ... below 64 for dilation s < 64
   const int32_t* row_ptr;  // CSR of allowed tiles, device
   const int32_t* col;
   const uint8_t* cls;

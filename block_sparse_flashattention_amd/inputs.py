@@ -55,6 +55,9 @@ class Workload:
     out_f32: bool = False
     # quantiles of the eligible block maxima used to calibrate tau; () = no skipping
     tau_quantiles: tuple = field(default_factory=tuple)
+    # further static mask fields as (name, value) pairs: dilation, dilation_taps, block,
+    # random_ppm, random_seed
+    mask_extra: tuple = field(default_factory=tuple)
 
     @property
     def group(self) -> int:

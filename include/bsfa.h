@@ -53,16 +53,31 @@ typedef enum { BSFA_OUT_BF16 = 0, BSFA_OUT_F32 = 1 } bsfa_out_dtype;
 /* Block classes (bit flags in bsfa_block_lists.cls). */
 #define BSFA_CLS_PARTIAL 1u /* some element of the 64x64 tile is masked: test per element */
 #define BSFA_CLS_FORCED 2u  /* the gate never skips this tile                              */
+#define BSFA_CLS_RANDOM 4u  /* the random primitive selects this tile's 64-token blocks    */
 
 /*
  * Static sparsity primitives, OR-composed as in "SAS: Sparse Attention Synthesizer",
- * Step 5 (Logic Operators). Element (i, j), 0-based, with 0 <= i, j < N is allowed iff
- *   (!causal || j <= i) && (window == 0 || |i - j| < window || j < n_global || i < n_global).
- * With causal set, the window is the glossary page's [max(0, i - W + 1), i] ("Mistral/
- * Mixtral Sliding Window Attention"); global tokens follow "Global Tokens in Attention"
- * (the first tokens are visible to all, and see all). Forcing: the tile holding a
- * diagonal element (i, i) is never skipped when force_keep_diag != 0, and tiles holding
- * a key j < n_global are never skipped when force_keep_global != 0.
+ * Step 5 (Logic Operators), with the patterns of the "sparse attention mechanism"
+ * glossary (table "Sparse Attention Patterns"). Element (i, j), 0-based, 0 <= i, j < N,
+ * is allowed iff
+ *   (!causal || j <= i) && (no pattern primitive set || pattern(i, j))
+ * where pattern(i, j) is the OR of the primitives that are set:
+ *   window > 0        |i - j| < window   (causal: the glossary's "Mistral/Mixtral
+ *                     Sliding Window Attention" range [max(0, i - W + 1), i])
+ *   dilation > 0      (i - j) is a multiple of dilation ("every k-th token"), and, when
+ *                     dilation_taps > 0, |i - j| < dilation * dilation_taps
+ *   block > 0         i / block == j / block ("attend within fixed-size blocks")
+ *   random_ppm > 0    the 64-token blocks (i / 64, j / 64) are chosen by the random
+ *                     primitive (BigBird's random attention): SplitMix64 of the counter
+ *                     (random_seed mod 2^24) * 2^40 + (i / 64) * 2^20 + (j / 64), kept
+ *                     when its top 32 bits are below floor(random_ppm * 2^32 / 10^6)
+ *   n_global > 0      j < n_global or i < n_global ("Global Tokens in Attention": the
+ *                     first tokens are visible to all, and see all); with no other
+ *                     primitive set this changes nothing
+ * Forcing: the tile holding a diagonal element (i, i) is never skipped when
+ * force_keep_diag != 0, and tiles holding a key j < n_global are never skipped when
+ * force_keep_global != 0. Field limits: window, n_global, dilation, dilation_taps,
+ * block >= 0; 0 <= random_ppm <= 1000000; random_seed any.
  */
 typedef struct {
   int32_t causal;
@@ -70,6 +85,11 @@ typedef struct {
   int32_t n_global;
   int32_t force_keep_diag;
   int32_t force_keep_global;
+  int32_t dilation;
+  int32_t dilation_taps;
+  int32_t block;
+  int32_t random_ppm;
+  int32_t random_seed;
 } bsfa_mask_spec;
 
 /* Element strides of a [B, H, N, d] tensor; the d dimension must be contiguous. */
@@ -156,7 +176,7 @@ int bsfa_skip_stats(const uint64_t* stats_dev, int32_t B, int32_t Hq, uint64_t* 
 /* Thread-local text for the last failing call on this thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2). */
 int32_t bsfa_abi_version(void);
 
 #ifdef __cplusplus

@@ -36,6 +36,18 @@ Readings taken where the pages leave a step open (each is also listed in DESIGN.
 * The window is |i - j| < W; with the causal mask this is the page's [i - W + 1, i].
   Global tokens act on both sides: keys j < n_global are seen by every query, and
   queries i < n_global see every key; the causal mask still applies (AND).
+* The glossary's other static patterns ("sparse attention mechanism", table "Sparse
+  Attention Patterns") are read as OR-able primitives:
+  - dilated/strided ("every k-th token"): key j is allowed when i - j is a multiple of
+    the stride k, and, with w taps, |i - j| < k * w (no limit when w = 0);
+  - blockwise ("within fixed-size blocks"): i and j lie in the same block of B tokens,
+    floor(i / B) == floor(j / B);
+  - BigBird's random part: whole 64-token blocks (query block t, key block c) chosen at
+    random with a given rate. The choice is SplitMix64 (Steele, Lea and Flood, "Fast
+    splittable pseudorandom number generators", 2014) of a counter built from (seed, t,
+    c), keeping the block when the top 32 output bits fall below the rate's threshold.
+  With no pattern primitive at all every pair is allowed (then global tokens change
+  nothing).
 * A query with no kept key gets O = 0 and LSE = -inf.
 * The block size is a parameter (64 x 64 on the GPU); block size 1 turns the rule into
   an element-level one, which lets the pages' small worked examples run through it.
@@ -57,13 +69,52 @@ class MaskSpec:
     n_global: int = 0  # keys j < n_global and queries i < n_global are global
     force_keep_diag: bool = True
     force_keep_global: bool = True
+    dilation: int = 0  # 0: off; else i - j must be a multiple of this stride (>= 2)
+    dilation_taps: int = 0  # with a stride: |i - j| < stride * taps (0: no limit)
+    block: int = 0  # 0: off; else i and j in the same block of this many tokens
+    random_ppm: int = 0  # random 64-token blocks, rate in parts per million (0: off)
+    random_seed: int = 0
+
+    @property
+    def has_pattern(self) -> bool:
+        return (self.window > 0 or self.dilation > 0 or self.block > 0
+                or self.random_ppm > 0)
+
+
+RANDOM_BLOCK = 64  # granularity of the random primitive (tokens)
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """SplitMix64 output for counter x (Steele, Lea and Flood, 2014): add the golden-
+    ratio increment, then the variant-13 finaliser of MurmurHash3's mixer."""
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def random_block_selected(seed: int, t: int, c: int, ppm: int) -> bool:
+    """Whether the random primitive selects 64-token query block t x key block c.
+
+    Counter = seed * 2^40 + t * 2^20 + c (t, c < 2^20); selected when the top 32 bits of
+    SplitMix64(counter) are below floor(ppm * 2^32 / 10^6)."""
+    seed, t, c, ppm = int(seed), int(t), int(c), int(ppm)  # exact integer arithmetic
+    if ppm <= 0:
+        return False
+    counter = ((seed & 0xFFFFFF) << 40) | ((t & 0xFFFFF) << 20) | (c & 0xFFFFF)
+    threshold = (ppm * (1 << 32)) // 1_000_000
+    return (splitmix64(counter) >> 32) < threshold
 
 
 def element_mask(rows, cols, n: int, spec: MaskSpec) -> np.ndarray:
     """Static mask A(i, j) for query rows ``rows`` and key columns ``cols``.
 
-    A(i, j) = [0 <= i, j < n] and [not causal or j <= i] and
-              [no window or |i - j| < W or j < n_global or i < n_global].
+    A(i, j) = [0 <= i, j < n] and [not causal or j <= i] and pattern(i, j), where the
+    pattern is all pairs when no pattern primitive is set, else the OR of
+      |i - j| < W (window),  (i - j) % k == 0 with |i - j| < k * taps (dilated),
+      i // B == j // B (blockwise),  random 64-token block (i // 64, j // 64),
+      j < n_global or i < n_global (global tokens).
     """
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.asarray(cols, dtype=np.int64)[None, :]
@@ -72,12 +123,28 @@ def element_mask(rows, cols, n: int, spec: MaskSpec) -> np.ndarray:
         causal_ok = j <= i
     else:
         causal_ok = np.ones(inside.shape, dtype=bool)
+    if not spec.has_pattern:
+        return inside & causal_ok
+    pattern = (j < spec.n_global) | (i < spec.n_global)
     if spec.window > 0:
-        band = np.abs(i - j) < spec.window
-        glob = (j < spec.n_global) | (i < spec.n_global)
-        pattern = band | glob
-    else:
-        pattern = np.ones(inside.shape, dtype=bool)
+        pattern = pattern | (np.abs(i - j) < spec.window)
+    if spec.dilation > 0:
+        dil = (i - j) % spec.dilation == 0
+        if spec.dilation_taps > 0:
+            dil = dil & (np.abs(i - j) < spec.dilation * spec.dilation_taps)
+        pattern = pattern | dil
+    if spec.block > 0:
+        pattern = pattern | (i // spec.block == j // spec.block)
+    if spec.random_ppm > 0:
+        # decide each (query block, key block) pair once, then spread it to its elements
+        tb, ti = np.unique(np.asarray(rows, dtype=np.int64) // RANDOM_BLOCK,
+                           return_inverse=True)
+        cb, ci = np.unique(np.asarray(cols, dtype=np.int64) // RANDOM_BLOCK,
+                           return_inverse=True)
+        sel = np.array([[random_block_selected(spec.random_seed, int(t), int(c),
+                                               spec.random_ppm) for c in cb] for t in tb],
+                       dtype=bool).reshape(len(tb), len(cb))
+        pattern = pattern | sel[ti.reshape(-1)[:, None], ci.reshape(-1)[None, :]]
     return inside & causal_ok & pattern
 
 

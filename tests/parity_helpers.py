@@ -36,13 +36,15 @@ def f64(bits: np.ndarray) -> np.ndarray:
 
 
 def oracle_spec(w: inputs.Workload) -> orc.MaskSpec:
-    return orc.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
+    return orc.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global,
+                        **dict(w.mask_extra))
 
 
 def gpu_spec(w: inputs.Workload):
     import block_sparse_flashattention_amd as bsfa
 
-    return bsfa.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
+    return bsfa.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global,
+                         **dict(w.mask_extra))
 
 
 def reduced(w: inputs.Workload, qb, kb, vb, heads):

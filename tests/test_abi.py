@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
                           "bsfa_last_error", "bsfa_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.bsfa_abi_version() == 1
+    assert lib.bsfa_abi_version() == 2
 
 
 def test_two_call_sizing_and_too_small():

@@ -17,7 +17,17 @@ SPECS = [
     dict(causal=True, window=3, n_global=1),
     dict(causal=False, window=200, n_global=130),
     dict(causal=True, window=0, n_global=128),
+    # the dilated, blockwise and random primitives, alone and OR-composed
+    dict(causal=True, dilation=3, dilation_taps=40),
+    dict(causal=False, dilation=70),
+    dict(causal=True, dilation=64, dilation_taps=5, n_global=10),
+    dict(causal=True, block=100),
+    dict(causal=False, block=64, n_global=3),
+    dict(causal=True, random_ppm=300_000, random_seed=4),
+    dict(causal=False, window=30, dilation=9, dilation_taps=7, block=150,
+         random_ppm=100_000, random_seed=123, n_global=2),
 ]
+EXTRA = SPECS[9:]
 
 
 def _check(spec_kw, n, bq, bk, diag=True, glob=True):
@@ -38,6 +48,9 @@ def _check(spec_kw, n, bq, bk, diag=True, glob=True):
         for e, c in zip(range(row_ptr[t], row_ptr[t + 1]), cols):
             assert bool(cls[e] & 1) == (not all_allowed[t, c]), (t, c)
             assert bool(cls[e] & 2) == bool(forced[c]), (t, c)
+            if bq == 64 and bk == 64:
+                rnd = orc.random_block_selected(om.random_seed, t, c, om.random_ppm)
+                assert bool(cls[e] & 4) == rnd, (t, c)
 
 
 @pytest.mark.parametrize("spec_kw", SPECS)
@@ -46,10 +59,17 @@ def test_lists_match_element_mask_64(spec_kw, n):
     _check(spec_kw, n, 64, 64)
 
 
-@pytest.mark.parametrize("spec_kw", SPECS[:6])
-@pytest.mark.parametrize("bq,bk", [(1, 1), (2, 3), (16, 8), (64, 32)])
+@pytest.mark.parametrize("spec_kw", SPECS[:6] + EXTRA)
+@pytest.mark.parametrize("bq,bk", [(1, 1), (2, 3), (16, 8), (64, 32), (100, 130)])
 def test_lists_match_element_mask_other_blocks(spec_kw, bq, bk):
-    _check(spec_kw, 97, bq, bk)
+    _check(spec_kw, 197, bq, bk)
+
+
+def test_invalid_primitive_fields():
+    for bad in (dict(dilation=-1), dict(block=-2), dict(dilation_taps=-3),
+                dict(random_ppm=-1), dict(random_ppm=1_000_001)):
+        with pytest.raises(bsfa.BsfaError):
+            bsfa.build_block_lists(bsfa.MaskSpec(**bad), 128)
 
 
 @pytest.mark.parametrize("diag,glob", list(itertools.product([False, True], repeat=2)))
