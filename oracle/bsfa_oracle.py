@@ -363,3 +363,103 @@ def calibrate_tau(
         vals = np.concatenate(per_head[h]) if per_head[h] else np.empty(0)
         taus[h] = np.quantile(vals, quantile) if vals.size else -np.inf
     return taus
+
+
+# ---------------------------------------------------------------------------------------
+# Decode (token generation): one new query row per sequence and query head against a
+# key/value cache.
+#
+# The pages describe token generation as one new token at a time over a cache of the
+# keys and values of all earlier tokens ("SAS: Sparse Attention Synthesizer", Challenge 2
+# "KV Cache Management" and Step 6), and the block gate for prefill ("Block Sparse Flash
+# Attention", "The paper's summary"). Reading taken for decode (listed in the design doc):
+# the query tile is that single row. Each 64-key block of the cache gets the maximum of
+# the row's scaled scores over its allowed keys. The block is kept when forced (it holds
+# the row's own key, or a global key) or when that maximum is >= tau_h. The output is
+# the renormalised softmax over the kept keys, as in prefill. The row's position is the
+# newest token, lengths[b] - 1, and its own key and value are already in the cache.
+# Lengths above the cache size count as the cache size. A length <= 0 leaves the row
+# with no keys: O = 0, LSE = -inf.
+# ---------------------------------------------------------------------------------------
+
+
+@dataclass
+class DecodeResult:
+    out: np.ndarray  # [B, Hq, dv]
+    lse: np.ndarray  # [B, Hq]
+    tile_max: np.ndarray  # [B, Hq, nkb]; -inf where not allowed
+    keep: np.ndarray  # [B, Hq, nkb]
+    allowed: np.ndarray  # [B, nkb]
+    forced: np.ndarray  # [B, nkb]; forced and allowed
+
+
+def decode(q, k_cache, v_cache, lengths, spec: MaskSpec, tau=None, block_k: int = 64,
+           scale: float | None = None, keep_override=None) -> DecodeResult:
+    """BSFA decode step on the CPU in fp64.
+
+    q: [B, Hq, d], the newest token's query per sequence and head; k_cache: [B, Hkv,
+    Lmax, d]; v_cache: [B, Hkv, Lmax, dv]; lengths: [B] valid cache rows per sequence.
+    tau: None (dense path), a scalar, or one value per query head. keep_override:
+    optional bool [B, Hq, nkb] replacing the gate's decisions. Blocks are counted over
+    the cache size: nkb = ceil(Lmax / block_k).
+    """
+    q = np.asarray(q)
+    k_cache = np.asarray(k_cache)
+    v_cache = np.asarray(v_cache)
+    bsz, hq, d = q.shape
+    hkv, lmax = k_cache.shape[1], k_cache.shape[2]
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nkb = tile_grid(lmax, block_k)
+    taus = [None] * hq if tau is None else [
+        float(x) for x in np.broadcast_to(np.asarray(tau, dtype=np.float64), (hq,))]
+    dv = v_cache.shape[3]
+    out = np.zeros((bsz, hq, dv))
+    lse = np.full((bsz, hq), -np.inf)
+    tmax = np.full((bsz, hq, nkb), -np.inf)
+    keep = np.zeros((bsz, hq, nkb), dtype=bool)
+    allowed_all = np.zeros((bsz, nkb), dtype=bool)
+    forced_all = np.zeros((bsz, nkb), dtype=bool)
+    for b in range(bsz):
+        n = min(int(lengths[b]), lmax)
+        if n <= 0:
+            continue
+        i = n - 1  # the new token's position
+        nb = tile_grid(n, block_k)
+        a_panel = element_mask([i], np.arange(n), n, spec)
+        forced = forced_tiles(i, n, spec, 1, block_k)  # query tile = the single row i
+        for h in range(hq):
+            g = h // group
+            s_panel = scores(q[b, h][None, :], k_cache[b, g, :n], scale)
+            m, allowed = tile_max(s_panel, a_panel, block_k)
+            if keep_override is not None:
+                kp = np.asarray(keep_override[b, h, :nb], dtype=bool) & allowed
+            else:
+                kp = keep_tiles(m, allowed, forced, taus[h])
+            o, l = combine(s_panel, a_panel, kp, v_cache[b, g, :n], block_k)
+            out[b, h] = o[0]
+            lse[b, h] = l[0]
+            tmax[b, h, :nb] = m
+            keep[b, h, :nb] = kp
+            allowed_all[b, :nb] = allowed
+            forced_all[b, :nb] = forced & allowed
+    return DecodeResult(out, lse, tmax, keep, allowed_all, forced_all)
+
+
+def calibrate_tau_decode(q, k_cache, lengths, spec: MaskSpec, quantile: float,
+                         block_k: int = 64, scale: float | None = None) -> np.ndarray:
+    """Decode thresholds, one per query head: the ``quantile`` (numpy's default linear
+    interpolation) of head h's eligible block maxima (allowed, not forced) of the decode
+    rows on calibration inputs, as for prefill but with the single-row query tile."""
+    r = decode(q, k_cache, v_cache=np.zeros(np.asarray(k_cache).shape[:3] + (1,)),
+               lengths=lengths, spec=spec, tau=None, block_k=block_k, scale=scale)
+    hq = r.tile_max.shape[1]
+    taus = np.empty(hq)
+    for h in range(hq):
+        eligible = r.allowed & ~r.forced
+        vals = r.tile_max[:, h][eligible]
+        taus[h] = np.quantile(vals, quantile) if vals.size else -np.inf
+    return taus
