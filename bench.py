@@ -13,6 +13,7 @@ is reported separately. Inputs are resident in HBM before the timed region start
 Prints ONE JSON line (metric, value in executed TFLOP/s, roofline, cpu_baseline, ...).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+       python bench.py --workload decode_sink_local_64k   (the decode step instead)
        python bench.py --copy-probe        (a plain copy of known size, for counters)
 """
 from __future__ import annotations
@@ -34,7 +35,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_flashattention_amd", "csrc", f)
-                  for f in ("bsfa_fwd.hip", "bsfa_host.cpp", "bsfa_internal.h")]
+                  for f in ("bsfa_fwd.hip", "bsfa_device.h", "bsfa_host.cpp",
+                            "bsfa_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsfa_fwd_gated_sink_local_64k_traffic.json")
 
 
@@ -61,6 +63,29 @@ def measured_traffic():
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+DECODE_SOURCES = [os.path.join(ROOT, "block_sparse_flashattention_amd", "csrc", f)
+                  for f in ("bsfa_decode.hip", "bsfa_device.h", "bsfa_host.cpp",
+                            "bsfa_internal.h")]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsfa_decode_sink_local_64k_traffic.json")
+
+
+def measured_decode_traffic():
+    """HBM bytes per decode step (both kernels) from the committed counter summary, if it
+    was taken on the current decode source; else None."""
+    try:
+        with open(DECODE_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    if rec.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return rec.get("hbm_bytes_per_step")
 
 
 def tile_flops(d: int):
@@ -144,6 +169,167 @@ def cpu_baseline(w, taus_gpu_unused, budget_s: float = 20.0):
     }
 
 
+def decode_bytes(w, lengths, keep=None):
+    """Algorithmic HBM bytes of one decode step: the new query rows, the K rows of every
+    allowed block, the V rows of every block some query head of its KV group keeps (all
+    allowed blocks on the dense path), O and LSE. ``keep``: bool [B, Hq, nkb] or None."""
+    nkb = -(-w.Lmax // 64)
+    row = w.d * 2
+    total = w.B * w.Hq * w.d * 2 + w.B * w.Hq * w.d * (4 if w.out_f32 else 2) + w.B * w.Hq * 4
+    for b in range(w.B):
+        n = min(max(int(lengths[b]), 0), w.Lmax)
+        rows = np.array([max(0, min(64, n - c * 64)) for c in range(nkb)])
+        total += w.Hkv * int(rows.sum()) * row  # K (causal, no pattern: every block < n)
+        if keep is None:
+            total += w.Hkv * int(rows.sum()) * row
+        else:
+            kg = keep[b].reshape(w.Hkv, w.group, nkb).any(axis=1)  # [Hkv, nkb]
+            total += int((kg * rows[None, :]).sum()) * row
+    return total
+
+
+def cpu_baseline_decode(w, lengths, budget_s: float = 20.0):
+    """Time the fp64 CPU oracle's decode step on the same workload (whole sequences,
+    one at a time, until the budget is spent)."""
+    from block_sparse_flashattention_amd import inputs
+    from oracle import bsfa_oracle as orc
+
+    cores = len(os.sched_getaffinity(0))
+    spec = orc.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
+    f64 = lambda bits: inputs.bits_to_f32(bits).astype(np.float64)
+    qc, kc, _, lc = inputs.generate_decode(w, 1)
+    taus = orc.calibrate_tau_decode(f64(qc[:1]), f64(kc[:1]), lc[:1], spec, 0.5)
+    del qc, kc
+    qb, kb, vb, _ = inputs.generate_decode(w, 0)
+    done, nbytes, elapsed = 0, 0, 0.0
+    for b in range(w.B):
+        q, k, v = f64(qb[b:b + 1]), f64(kb[b:b + 1]), f64(vb[b:b + 1])
+        t0 = time.perf_counter()
+        r = orc.decode(q, k, v, lengths[b:b + 1], spec, tau=taus)
+        elapsed += time.perf_counter() - t0
+        sub = inputs.scaled(w, B=1, lengths=(int(lengths[b]),))
+        nbytes += decode_bytes(sub, lengths[b:b + 1], r.keep)
+        done += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": nbytes / elapsed / 1e9,
+        "unit": "GB/s (algorithmic bytes)",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done} of {w.B} sequences of the same workload, every head, taus from "
+                   f"the oracle's own calibration on sequence 0 of the calibration seed; "
+                   f"{elapsed:.1f} s of fp64 numpy"),
+        "elapsed_s": elapsed,
+    }
+
+
+def bench_decode(args, w):
+    """Decode step: one new query row per sequence and head against the cache."""
+    import torch
+
+    import block_sparse_flashattention_amd as bsfa
+    from block_sparse_flashattention_amd import inputs
+
+    dev = torch.device("cuda:0")
+    mask = bsfa.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)
+    out_dtype = torch.float32 if w.out_f32 else torch.bfloat16
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.perf_counter()
+    qc, kc, _, lc = inputs.generate_decode(w, 1)
+    taus = bsfa.decode_calibrate_tau(to_dev(qc), to_dev(kc), torch.tensor(lc, device=dev),
+                                     mask, args.quantile)
+    del qc, kc
+    qb, kb, vb, lengths = inputs.generate_decode(w, 0)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    lens = torch.tensor(lengths, device=dev)
+    del qb, kb, vb
+    torch.cuda.synchronize()
+    log(f"[bench] decode inputs resident and tau calibrated in {time.perf_counter() - t0:.1f} s")
+
+    out = torch.empty((w.B, w.Hq, w.d), dtype=out_dtype, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsfa.decode_workspace_size(w.B, w.Hq, w.Lmax, w.d), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    tau_t = torch.tensor(taus, dtype=torch.float32, device=dev)
+
+    def timed(tt, label):
+        for _ in range(args.warmup):
+            bsfa.decode(q, k, v, lens, mask=mask, tau=tt, out=out, lse_out=lse, workspace=ws,
+                        stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t_start = time.perf_counter()
+        for s_, e_ in evs:
+            s_.record(stream)
+            bsfa.decode(q, k, v, lens, mask=mask, tau=tt, out=out, lse_out=lse, workspace=ws,
+                        stream=stream.cuda_stream)
+            e_.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_start) / args.steps * 1e3
+        kern = float(np.mean([s_.elapsed_time(e_) for s_, e_ in evs]))
+        log(f"[bench] {label}: {wall:.4f} ms/step, kernels {kern:.4f} ms")
+        return wall, kern
+
+    dense_ms, dense_kern = timed(None, "dense decode (tau=NULL)")
+    gated_ms, gated_kern = timed(tau_t, f"gated decode tau@q={args.quantile}")
+    res = bsfa.decode(q, k, v, lens, mask=mask, tau=tau_t, out=out, lse_out=lse, workspace=ws,
+                      stats=True, export_tiles=True)
+    torch.cuda.synchronize()
+    keep = res.keep.cpu().numpy().astype(bool)
+    st = res.stats.cpu().numpy()
+    kept, skipped = int(st[..., 0].sum()), int(st[..., 1].sum())
+    tmax = res.tile_max.cpu().numpy()
+    allowed = tmax > -np.inf
+    nkb = keep.shape[2]
+    any_keep = keep.reshape(w.B, w.Hkv, w.group, nkb).any(axis=2)
+    allowed_g = allowed.reshape(w.B, w.Hkv, w.group, nkb).any(axis=2)
+    gated_bytes = decode_bytes(w, lengths, keep)
+    dense_bytes = decode_bytes(w, lengths, None)
+    value = gated_bytes / (gated_ms / 1e3) / 1e9
+    achieved = gated_bytes / (gated_kern / 1e3) / 1e9
+    line = {
+        "metric": "BSFA decode step, algorithmic HBM GB/s (one new token per sequence)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gated_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lmax": w.Lmax,
+                   "lengths": list(map(int, lengths)), "d": w.d, "mask": "causal",
+                   "tau_quantile": args.quantile, "block": "1x64"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_decode_traffic()},
+        "tokens_per_s": round(w.B / (gated_ms / 1e3), 1),
+        "dense_path_ms": round(dense_ms, 5),
+        "dense_path_gbs": round(dense_bytes / (dense_kern / 1e3) / 1e9, 1),
+        "speedup_vs_dense": round(dense_ms / gated_ms, 4),
+        "skip_fraction_allowed": round(skipped / max(kept + skipped, 1), 4),
+        "v_blocks_skipped_fraction": round(1 - any_keep.sum() / max(allowed_g.sum(), 1), 4),
+        "kernel_ms_mean": round(gated_kern, 5),
+        "algorithmic_bytes_per_step": gated_bytes,
+        "dense_bytes_per_step": dense_bytes,
+    }
+    if not args.no_cpu_baseline:
+        del q, k, v
+        torch.cuda.empty_cache()
+        log("[bench] timing the CPU oracle's decode")
+        line["cpu_baseline"] = cpu_baseline_decode(w, lengths, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +358,9 @@ def main():
     from block_sparse_flashattention_amd import inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload in inputs.DECODE_WORKLOADS:
+        bench_decode(args, inputs.DECODE_WORKLOADS[args.workload])
+        return
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
     mask = bsfa.MaskSpec(causal=w.causal, window=w.window, n_global=w.n_global)

@@ -78,6 +78,16 @@ def load_library():
         ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p]
     lib.bsfa_fwd.restype = ctypes.c_int
+    lib.bsfa_decode_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, P(ctypes.c_int64)]
+    lib.bsfa_decode_workspace_size.restype = ctypes.c_int
+    lib.bsfa_decode.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, P(_CStrides), P(_CStrides), P(_CStrides), P(_CStrides), P(_CMask),
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.bsfa_decode.restype = ctypes.c_int
     lib.bsfa_skip_stats.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.bsfa_skip_stats.restype = ctypes.c_int
@@ -250,6 +260,134 @@ def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0
     if tm is not None and lists.nnz == 0:
         tm, kp = tm[..., :0], kp[..., :0]
     return FwdResult(out, lse, st, tm, kp, lists)
+
+
+@dataclass
+class DecodeResult:
+    out: object  # [B, Hq, d]
+    lse: object  # fp32 [B, Hq]
+    stats: object = None  # int64 [B, Hq, 2] {kept, skipped} allowed blocks
+    tile_max: object = None  # fp32 [B, Hq, nkb]
+    keep: object = None  # uint8 [B, Hq, nkb]
+
+
+def decode_workspace_size(batch: int, hq: int, max_len: int, d: int) -> int:
+    """Bytes of scratch ``decode`` needs (bsfa_decode_workspace_size)."""
+    lib = load_library()
+    nbytes = ctypes.c_int64(0)
+    _check(lib, lib.bsfa_decode_workspace_size(batch, hq, max_len, d, ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
+           softmax_scale: float = 0.0, out_dtype=None, out=None, want_lse: bool = True,
+           stats: bool = False, export_tiles: bool = False, workspace=None, stream=None,
+           lse_out=None, stats_out=None) -> DecodeResult:
+    """One block-sparse decode step on the GPU (asynchronous on the current stream).
+
+    q: bf16 [B, Hq, d], the newest token's query per sequence and head; k_cache, v_cache:
+    bf16 [B, Hkv, Lmax, d] (last dim contiguous); lengths: int32 [B] on the device, the
+    valid cache rows of each sequence (the new token is row lengths[b] - 1). tau: None
+    (dense path) or fp32 [Hq]. ``workspace`` is an optional caller buffer of at least
+    decode_workspace_size bytes (a uint8 tensor); one is allocated here otherwise.
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise BsfaError(-1, "q must be [B, Hq, d] and the caches [B, Hkv, Lmax, d]")
+    if (q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16
+            or v_cache.dtype != torch.bfloat16):
+        raise BsfaError(-2, "q, k_cache, v_cache must be bfloat16")
+    bsz, hq, d = q.shape
+    hkv, lmax = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (bsz, hkv, lmax, d) or tuple(v_cache.shape) != (bsz, hkv, lmax, d):
+        raise BsfaError(-1, f"shape mismatch q{tuple(q.shape)} k{tuple(k_cache.shape)} "
+                            f"v{tuple(v_cache.shape)}")
+    if lengths.dtype != torch.int32 or lengths.numel() != bsz or not lengths.is_contiguous():
+        raise BsfaError(-1, "lengths must be a contiguous int32 tensor of B values")
+    if q.stride(2) != 1:
+        raise BsfaError(-2, "the head dimension of q must be contiguous")
+    dev = q.device
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=out_dtype, device=dev)
+    if out.stride(2) != 1:
+        raise BsfaError(-2, "the head dimension of out must be contiguous")
+    if lse_out is not None:
+        lse = lse_out
+    else:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if want_lse else None
+    tau_t = None
+    if tau is not None:
+        tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
+        if tau_t.numel() == 1 and hq > 1:
+            tau_t = tau_t.expand(hq).contiguous()
+        if tau_t.numel() != hq:
+            raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
+        tau_t = tau_t.contiguous()
+    if stats_out is not None:
+        st = stats_out
+    else:
+        st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
+    nkb = -(-lmax // 64)
+    tm = kp = None
+    if export_tiles:
+        tm = torch.empty((bsz, hq, nkb), dtype=torch.float32, device=dev)
+        kp = torch.empty((bsz, hq, nkb), dtype=torch.uint8, device=dev)
+    need = decode_workspace_size(bsz, hq, lmax, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    cm = mask._c()
+    sq = _CStrides(q.stride(0), q.stride(1), 0)
+    so = _CStrides(out.stride(0), out.stride(1), 0)
+    sk, sv = _strides(k_cache), _strides(v_cache)
+    status = lib.bsfa_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, bsz, hq, hkv, lmax, d,
+        ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
+        ctypes.byref(cm), tau_t.data_ptr() if tau_t is not None else None,
+        float(softmax_scale), OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
+        st.data_ptr() if st is not None else None,
+        tm.data_ptr() if tm is not None else None,
+        kp.data_ptr() if kp is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    _check(lib, status)
+    return DecodeResult(out, lse, st, tm, kp)
+
+
+def decode_calibration_maxima(q, k_cache, lengths, mask: MaskSpec, softmax_scale: float = 0.0,
+                              stream=None):
+    """Eligible (allowed, not forced) decode block maxima per query head, from one
+    gate-only decode pass: with tau = NaN only forced blocks are kept, so the exported
+    keep bits mark exactly the forced blocks."""
+    import torch
+
+    hq = q.shape[1]
+    res = decode(q, k_cache, k_cache, lengths, mask=mask,
+                 tau=torch.full((hq,), math.nan, device=q.device),
+                 softmax_scale=softmax_scale, want_lse=False, export_tiles=True,
+                 stream=stream)
+    torch.cuda.synchronize(q.device)
+    tmax = res.tile_max.cpu().numpy()  # [B, Hq, nkb]
+    keep = res.keep.cpu().numpy().astype(bool)  # forced blocks only (tau = NaN)
+    allowed = tmax > -np.inf  # blocks with no allowed key export -inf
+    return [tmax[:, h][allowed[:, h] & ~keep[:, h]].reshape(-1) for h in range(hq)]
+
+
+def decode_calibrate_tau(q, k_cache, lengths, mask: MaskSpec, quantile,
+                         softmax_scale: float = 0.0, stream=None):
+    """Per-head decode thresholds: the ``quantile`` of the eligible decode block maxima
+    of each query head on calibration inputs (as ``calibrate_tau`` for prefill)."""
+    maxima = decode_calibration_maxima(q, k_cache, lengths, mask, softmax_scale, stream)
+    qs = np.atleast_1d(np.asarray(quantile, dtype=np.float64))
+    taus = np.empty((qs.size, len(maxima)), dtype=np.float32)
+    for h, vals in enumerate(maxima):
+        taus[:, h] = np.quantile(vals.astype(np.float64), qs) if vals.size else -np.inf
+    return taus[0] if np.ndim(quantile) == 0 else taus
 
 
 def skip_stats(stats_tensor, stream=None):

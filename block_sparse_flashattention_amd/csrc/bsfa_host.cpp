@@ -196,13 +196,19 @@ bool view_fits(const bsfa_strides* s, int32_t N, int32_t d) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Decode splits: one workgroup per bsfa::DEC_BPS key blocks of the cache.
+int32_t decode_splits(int32_t max_len) {
+  const int32_t nkb = (max_len + 63) / 64;
+  return (nkb + bsfa::DEC_BPS - 1) / bsfa::DEC_BPS;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* bsfa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t bsfa_abi_version(void) { return 2; }
+int32_t bsfa_abi_version(void) { return 3; }
 
 int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_q,
                            int32_t block_k, int32_t* row_ptr, int32_t* col, uint8_t* cls,
@@ -352,6 +358,107 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   a.keep = keep;
   const char* err = nullptr;
   int rc = bsfa::launch_fwd(a, d, hpack, out_dtype == BSFA_OUT_F32, stream, &err);
+  if (rc != BSFA_OK) return fail(rc, "%s", err ? err : "launch failed");
+  return ok();
+}
+
+int bsfa_decode_workspace_size(int32_t B, int32_t Hq, int32_t max_len, int32_t d,
+                               int64_t* bytes) {
+  if (!bytes) return fail(BSFA_ERR_INVALID_ARG, "bytes is required");
+  if (B < 0 || Hq < 1 || max_len < 1)
+    return fail(BSFA_ERR_INVALID_ARG, "need B >= 0, Hq >= 1, max_len >= 1");
+  if (d != 64 && d != 128) return fail(BSFA_ERR_UNSUPPORTED, "head dim %d (need 64 or 128)", d);
+  *bytes = (int64_t)B * Hq * decode_splits(max_len) * (d + 4) * (int64_t)sizeof(float);
+  return ok();
+}
+
+int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
+                int32_t Hkv, int32_t max_len, int32_t d, const bsfa_strides* sq,
+                const bsfa_strides* sk, const bsfa_strides* sv, const bsfa_strides* so,
+                const bsfa_mask_spec* mask, const float* tau, float softmax_scale,
+                int32_t out_dtype, uint64_t* stats, float* tile_max, uint8_t* keep,
+                void* workspace, int64_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || max_len < 1)
+    return fail(BSFA_ERR_INVALID_ARG, "need B >= 0, Hq >= 1, Hkv >= 1, max_len >= 1");
+  if (Hq % Hkv != 0) return fail(BSFA_ERR_INVALID_ARG, "Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
+  if (!mask) return fail(BSFA_ERR_INVALID_ARG, "mask is required");
+  if (!valid_mask(mask))
+    return fail(BSFA_ERR_INVALID_ARG,
+                "mask fields must be >= 0 and random_ppm at most 1000000");
+  if (out_dtype != BSFA_OUT_BF16 && out_dtype != BSFA_OUT_F32)
+    return fail(BSFA_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale))
+    return fail(BSFA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if ((tile_max == nullptr) != (keep == nullptr))
+    return fail(BSFA_ERR_INVALID_ARG, "tile_max and keep must be given together");
+  if (tile_max && !tau)
+    return fail(BSFA_ERR_INVALID_ARG, "the per-block export needs tau (the gated path)");
+  if (d != 64 && d != 128) return fail(BSFA_ERR_UNSUPPORTED, "head dim %d (need 64 or 128)", d);
+  if (Hq / Hkv > 32)
+    return fail(BSFA_ERR_UNSUPPORTED, "more than 32 query heads per KV head (%d)", Hq / Hkv);
+  if (B == 0) return ok();
+  if (!q || !k_cache || !v_cache || !lengths || !out || !workspace)
+    return fail(BSFA_ERR_INVALID_ARG,
+                "q, k_cache, v_cache, lengths, out and workspace are required");
+  if (!sq || !sk || !sv || !so) return fail(BSFA_ERR_INVALID_ARG, "strides are required");
+  if (!valid_strides(sq) || !valid_strides(sk) || !valid_strides(sv) || !valid_strides(so))
+    return fail(BSFA_ERR_UNSUPPORTED, "strides must be non-negative multiples of 8 elements");
+  if (!view_fits(sk, max_len, d) || !view_fits(sv, max_len, d))
+    return fail(BSFA_ERR_UNSUPPORTED, "the K or V rows of one head span 2^31 bytes or more");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return fail(BSFA_ERR_UNSUPPORTED,
+                "q, k_cache, v_cache, out and workspace must be 16-byte aligned");
+  if ((uintptr_t)lengths & 3u) return fail(BSFA_ERR_UNSUPPORTED, "lengths must be 4-byte aligned");
+  const int32_t nsplit = decode_splits(max_len);
+  const int64_t need = (int64_t)B * Hq * nsplit * (d + 4) * (int64_t)sizeof(float);
+  if (workspace_bytes < need)
+    return fail(BSFA_ERR_BUFFER_TOO_SMALL, "workspace %lld bytes < %lld",
+                (long long)workspace_bytes, (long long)need);
+  if ((int64_t)B * Hkv * nsplit > INT32_MAX || (int64_t)B * Hq > INT32_MAX)
+    return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+
+  bsfa::DecArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.lengths = lengths;
+  a.out = out;
+  a.lse = lse;
+  a.ws = (float*)workspace;
+  a.sqb = sq->b; a.sqh = sq->h;
+  a.skb = sk->b; a.skh = sk->h; a.skn = sk->n;
+  a.svb = sv->b; a.svh = sv->h; a.svn = sv->n;
+  a.sob = so->b; a.soh = so->h;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lmax = max_len;
+  a.group = Hq / Hkv;
+  a.nkb = (max_len + 63) / 64;
+  a.nsplit = nsplit;
+  a.causal = mask->causal != 0;
+  a.window = mask->window;
+  a.n_global = mask->n_global;
+  a.pattern = has_pattern(*mask) ? 1 : 0;
+  a.dilation = mask->dilation;
+  a.block = mask->block;
+  a.dil_span = mask->dilation_taps > 0
+                   ? (int32_t)std::min<int64_t>((int64_t)mask->dilation * mask->dilation_taps,
+                                                INT32_MAX)
+                   : 0;
+  a.random_ppm = mask->random_ppm;
+  a.random_seed = mask->random_seed;
+  a.force_diag = mask->force_keep_diag != 0;
+  a.force_global = mask->force_keep_global != 0;
+  a.dil_bits = stride_pattern(mask->dilation);
+  a.tau = tau;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)d);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.stats = (unsigned long long*)stats;
+  a.tile_max = tile_max;
+  a.keep = keep;
+  const char* err = nullptr;
+  const int rc = bsfa::launch_decode(a, d, out_dtype == BSFA_OUT_F32, stream, &err);
   if (rc != BSFA_OK) return fail(rc, "%s", err ? err : "launch failed");
   return ok();
 }

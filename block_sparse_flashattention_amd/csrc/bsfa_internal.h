@@ -37,6 +37,42 @@ struct FwdArgs {
   uint8_t* keep;              // [B*Hq*nnz] or null
 };
 
+// Everything one decode launch needs: one new query row per (sequence, query head)
+// against a key/value cache, in splits of DEC_BPS key blocks per workgroup.
+constexpr int DEC_BPS = 4;  // 64-key blocks per split (one workgroup)
+
+struct DecArgs {
+  const uint16_t* q;        // bf16 bits [B, Hq, d]
+  const uint16_t* k;        // bf16 bits [B, Hkv, Lmax, d]
+  const uint16_t* v;        // bf16 bits [B, Hkv, Lmax, d]
+  const int32_t* lengths;   // [B], valid cache rows per sequence (clamped to [0, Lmax])
+  void* out;                // bf16 or fp32 [B, Hq, d]
+  float* lse;               // fp32 [B, Hq] or null
+  float* ws;                // per-split partials [B, Hq, nsplit, d + 1]
+  int64_t sqb, sqh;
+  int64_t skb, skh, skn;
+  int64_t svb, svh, svn;
+  int64_t sob, soh;
+  int32_t B, Hq, Hkv, Lmax;
+  int32_t group;            // Hq / Hkv, at most 32
+  int32_t nkb;              // ceil(Lmax / 64)
+  int32_t nsplit;           // ceil(nkb / DEC_BPS)
+  int32_t causal, window, n_global;
+  int32_t pattern;          // some pattern primitive is set (else all pairs pass)
+  int32_t dilation, block, dil_span;
+  int32_t random_ppm, random_seed;
+  int32_t force_diag, force_global;
+  unsigned long long dil_bits;
+  const float* tau;         // [Hq] or null (dense path)
+  float scale, scale_log2;
+  unsigned long long* stats;  // [B*Hq*2] or null
+  float* tile_max;            // [B*Hq*nkb] or null
+  uint8_t* keep;              // [B*Hq*nkb] or null
+};
+
+// Launches the decode split kernel and the combine kernel on `stream`.
+int launch_decode(const DecArgs& a, int d, bool out_f32, void* stream, const char** err);
+
 // Launches the forward kernel variant for head dim d, head pack hpack (query heads of
 // one KV group sharing a workgroup), gated (tau != null) or dense, bf16 or fp32 output.
 // Returns 0 or a negative bsfa_status; *err receives a static message on failure.

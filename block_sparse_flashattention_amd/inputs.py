@@ -30,6 +30,7 @@ Workload kinds:
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -178,8 +179,120 @@ def generate(w: Workload, seed: int, groups=None):
     return q, k, v
 
 
-def scaled(w: Workload, **changes) -> Workload:
-    """A copy of a workload with some fields replaced (e.g. a smaller N for tests)."""
+# ---------------------------------------------------------------------------------------
+# Decode workloads: one new query row per (sequence, query head) against a key/value cache
+# of Lmax rows, of which lengths[b] are valid; the new token is row lengths[b] - 1.
+# Streams: tensor ids 5 (new query rows), 6 (K cache), 7 (V cache), 8 (planted blocks).
+# The structure vectors are the prefill ones (structure seed 1000), so a decode workload
+# of a kind has the same "model" as the prefill workload of that kind:
+# * sink_local: q = z + mu_g + alpha R(p) c_g at the row's position p, the cache
+#   K_j = z'_j + alpha R(j) c_g; K row 0 is shifted by 3 times the mean of the group's
+#   new (bf16) query rows (the attention sink).
+# * planted: K = N(0,1) + 2.0 u_g on a random fraction of the 64-token blocks of the
+#   cache; q = N(0,1) + 1.5 u_g.
+# * gaussian: all N(0, 1).
+# ---------------------------------------------------------------------------------------
+TID_DQ, TID_DK, TID_DV, TID_DBLOCKS = 5, 6, 7, 8
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lmax: int
+    d: int
+    lengths: tuple  # valid cache rows per sequence
+    kind: str = "gaussian"
+    causal: bool = True
+    window: int = 0
+    n_global: int = 0
+    planted_frac: float = 0.0
+    out_f32: bool = False
+    tau_quantiles: tuple = field(default_factory=tuple)
+    mask_extra: tuple = field(default_factory=tuple)
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+
+DECODE_WORKLOADS = {
+    # four sequences of ragged lengths over a 64K-row cache, Llama-70B-like GQA heads
+    "decode_sink_local_64k": DecodeWorkload(
+        "decode_sink_local_64k", 4, 32, 8, 65536, 128,
+        lengths=(65536, 57345, 49150, 40961), kind="sink_local", tau_quantiles=(0.5,)),
+}
+
+
+def generate_decode_group(w: DecodeWorkload, seed: int, b: int, g: int, rot=None):
+    """New query rows of KV head g's query heads and its caches, as bf16 bits.
+
+    Returns (q_bits [group, d], k_bits [Lmax, d], v_bits [Lmax, d]). ``rot`` may pass
+    alpha * R(j) c_g for all cache rows (it depends on g only) to skip recomputing it.
+    """
+    lmax, d, grp = w.Lmax, w.d, w.group
+    p = max(int(w.lengths[b]) - 1, 0)
+    heads = range(g * grp, (g + 1) * grp)
+    q = np.stack([_rng(seed, TID_DQ, b, h).standard_normal(d, dtype=np.float32)
+                  for h in heads])
+    k = _rng(seed, TID_DK, b, g).standard_normal((lmax, d), dtype=np.float32)
+    v = _rng(seed, TID_DV, b, g).standard_normal((lmax, d), dtype=np.float32)
+    if w.kind == "planted":
+        u = _unit((STRUCTURE_SEED, SID_U, g), d)
+        nblk = (lmax + 63) // 64
+        count = int(round(w.planted_frac * nblk))
+        chosen = _rng(seed, TID_DBLOCKS, b, g).choice(nblk, size=count, replace=False)
+        for blk in chosen:
+            k[blk * 64:(blk + 1) * 64] += np.float32(2.0) * u
+        q += np.float32(1.5) * u
+    elif w.kind == "sink_local":
+        alpha = np.float32(3.0)
+        c = _unit((STRUCTURE_SEED, SID_C, g), d)
+        mu = _unit((STRUCTURE_SEED, SID_MU, g), d)
+        rc = alpha * _rotated(c, lmax) if rot is None else rot
+        q += mu
+        q += rc[p][None]
+        k += rc
+    elif w.kind != "gaussian":
+        raise ValueError(f"unknown workload kind {w.kind!r}")
+    q_bits = f32_to_bf16_bits(q)
+    if w.kind == "sink_local":
+        qmean = bits_to_f32(q_bits).astype(np.float64).mean(axis=0)
+        k[0] += (3.0 * qmean).astype(np.float32)
+    return q_bits, f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def generate_decode(w: DecodeWorkload, seed: int):
+    """Whole decode workload: q_bits [B, Hq, d], k_bits and v_bits [B, Hkv, Lmax, d],
+    lengths int32 [B]."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    q = np.zeros((w.B, w.Hq, w.d), dtype=np.uint16)
+    k = np.zeros((w.B, w.Hkv, w.Lmax, w.d), dtype=np.uint16)
+    v = np.zeros((w.B, w.Hkv, w.Lmax, w.d), dtype=np.uint16)
+    rots = {}
+    if w.kind == "sink_local":
+        for g in range(w.Hkv):
+            rots[g] = np.float32(3.0) * _rotated(_unit((STRUCTURE_SEED, SID_C, g), w.d), w.Lmax)
+
+    def one(bg):
+        b, g = bg
+        qg, kg, vg = generate_decode_group(w, seed, b, g, rots.get(g))
+        q[b, g * w.group:(g + 1) * w.group] = qg
+        k[b, g] = kg
+        v[b, g] = vg
+
+    # independent streams per (b, g): the result does not depend on the order
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+        list(pool.map(one, [(b, g) for b in range(w.B) for g in range(w.Hkv)]))
+    return q, k, v, np.asarray(w.lengths, dtype=np.int32)
+
+
+def scaled(w, **changes):
+    """A copy of a (prefill or decode) workload with some fields replaced (e.g. a
+    smaller N for tests)."""
     fields = {f: getattr(w, f) for f in w.__dataclass_fields__}
     fields.update(changes)
-    return Workload(**fields)
+    return type(w)(**fields)

@@ -1,5 +1,6 @@
 /*
- * bsfa.h -- C ABI of the block-sparse FlashAttention prefill library (libbsfa.so).
+ * bsfa.h -- C ABI of the block-sparse FlashAttention library (libbsfa.so): prefill
+ * (bsfa_fwd) and decode (bsfa_decode).
  *
  * What the library computes. For every batch b, query head h (key/value head
  * g = h / (Hq / Hkv), grouped-query sharing as in the "Multi-Query and Grouped-Query
@@ -44,7 +45,7 @@ typedef enum {
   BSFA_OK = 0,
   BSFA_ERR_INVALID_ARG = -1,      /* null pointer, negative size, inconsistent shapes   */
   BSFA_ERR_UNSUPPORTED = -2,      /* valid but not implemented (head dim, alignment)    */
-  BSFA_ERR_BUFFER_TOO_SMALL = -3, /* block-list capacity below the required entry count */
+  BSFA_ERR_BUFFER_TOO_SMALL = -3, /* a caller buffer (block lists, workspace) too small */
   BSFA_ERR_HIP = -4               /* a HIP runtime call failed; message has the reason  */
 } bsfa_status;
 
@@ -166,7 +167,70 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              void* stream);
 
 /*
- * Copy the per-(b, h) counters written by bsfa_fwd to the host and split them.
+ * Decode (token generation): one new query row per sequence b and query head h against
+ * a key/value cache. Token generation adds one token at a time and attends over the
+ * cached keys and values of all earlier tokens ("SAS: Sparse Attention Synthesizer",
+ * Challenge 2 "KV Cache Management" and Step 6). The gate is the one of bsfa_fwd with the
+ * single row as the query tile:
+ *   n      = min(lengths[b], max_len) valid cache rows; the row is the newest token,
+ *            position i = n - 1, whose own key and value are already cached
+ *   s_j    = scale * q . k_j for cached keys j < n; A(i, j) the static mask at row i
+ *   M_c    = max of s_j over the allowed keys of 64-key block c
+ *   keep_c = forced(c) OR M_c >= tau_h, forced(c): c holds key i (force_keep_diag) or a
+ *            key j < n_global (force_keep_global)
+ *   LSE    = log sum_{kept j} exp(s_j);  O = sum_{kept j} exp(s_j - LSE) v_j
+ * A V block is read only when some query head of its KV group keeps it. A row with no
+ * kept key (lengths[b] <= 0) gets O = 0 and LSE = -inf. Cache rows at or past n are never
+ * read (they may hold anything).
+ *
+ * The cache is split into groups of 4 blocks (256 keys); each (sequence, KV head, split)
+ * writes a partial (O_s, LSE_s) per head into the caller's workspace, and a second
+ * kernel merges them (LSE = log sum_s exp LSE_s, O = sum_s exp(LSE_s - LSE) O_s).
+ */
+
+/* Workspace bytes bsfa_decode needs: B * Hq * ceil(ceil(max_len / 64) / 4) * (d + 4) * 4.
+ * B >= 0, Hq >= 1, max_len >= 1, d in {64, 128}. */
+int bsfa_decode_workspace_size(int32_t B, int32_t Hq, int32_t max_len, int32_t d,
+                               int64_t* bytes);
+
+/*
+ * One decode step on the GPU, queued on `stream`.
+ *   q       : device bf16 [B, Hq, d]; row (b, h) at q + b * sq->b + h * sq->h (sq->n unused).
+ *   k_cache, v_cache: device bf16 [B, Hkv, max_len, d] with strides *sk, *sv. Hq % Hkv == 0
+ *             and Hq / Hkv <= 32.
+ *   lengths : device int32 [B], valid cache rows per sequence (values above max_len count
+ *             as max_len, values <= 0 as no rows). 4-byte aligned.
+ *   out     : device [B, Hq, d], bf16 or fp32 (out_dtype), strides *so (so->n unused).
+ *   lse     : device fp32 [B * Hq] (natural log); may be NULL.
+ *   max_len : cache rows, >= 1. d: 64 or 128.
+ *   mask    : static pattern (as for bsfa_fwd), evaluated at row i = n - 1.
+ *   tau     : device fp32 [Hq] in scaled-score units; NULL selects the dense path (every
+ *             allowed block kept). NaN keeps forced blocks only.
+ *   softmax_scale: 0 selects 1/sqrt(d).
+ *   stats   : device uint64 [B*Hq*2] = {kept, skipped} allowed blocks per (b, h), ADDED to
+ *             the buffer; may be NULL.
+ *   tile_max, keep: device fp32 / uint8 [B*Hq*nkb], nkb = ceil(max_len / 64): per (b, h,
+ *             block c) M_c (-inf where no key of the block is allowed or c >= ceil(n/64))
+ *             and the keep bit; both NULL or both set; needs tau != NULL.
+ *   workspace, workspace_bytes: device scratch of at least bsfa_decode_workspace_size
+ *             bytes, 16-byte aligned; its contents on entry do not matter. Calls that
+ *             share one workspace must not overlap in time.
+ * Pointers q, k_cache, v_cache, out must be 16-byte aligned and the used strides
+ * non-negative multiples of 8; the cache rows of one (sequence, KV head),
+ * ((max_len - 1) * n-stride + d) elements, must span fewer than 2^31 bytes.
+ * Errors: BSFA_ERR_BUFFER_TOO_SMALL for a short workspace, otherwise as bsfa_fwd.
+ */
+int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
+                int32_t Hkv, int32_t max_len, int32_t d, const bsfa_strides* sq,
+                const bsfa_strides* sk, const bsfa_strides* sv, const bsfa_strides* so,
+                const bsfa_mask_spec* mask, const float* tau, float softmax_scale,
+                int32_t out_dtype, uint64_t* stats, float* tile_max, uint8_t* keep,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Copy the per-(b, h) counters written by bsfa_fwd or bsfa_decode to the host and split
+ * them.
  *   stats_dev: device uint64 [B*Hq*2]; kept_host, skipped_host: host uint64 [B*Hq].
  * Synchronises `stream` before returning.
  */
@@ -176,7 +240,7 @@ int bsfa_skip_stats(const uint64_t* stats_dev, int32_t B, int32_t Hq, uint64_t* 
 /* Thread-local text for the last failing call on this thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* Library ABI version (this header: 2). */
+/* Library ABI version (this header: 3). */
 int32_t bsfa_abi_version(void);
 
 #ifdef __cplusplus

@@ -163,3 +163,91 @@ def run_gpu(w: inputs.Workload, qb, kb, vb, tau, export=True, stats=True, poison
                    stats=stats, export_tiles=export and tau is not None)
     torch.cuda.synchronize()
     return res
+
+
+# ---------------------------------------------------------------- decode (one new row)
+def decode_inputs(w, seed: int, poison_tail: bool = False):
+    """Decode inputs as bf16 bits; with ``poison_tail`` the cache rows at or past each
+    sequence's length hold NaN (free slots the kernel must never read)."""
+    qb, kb, vb, lengths = inputs.generate_decode(w, seed)
+    if poison_tail:
+        nan_bits = np.uint16(0x7FC0)
+        for b, n in enumerate(lengths):
+            n = max(int(n), 0)
+            kb[b, :, n:] = nan_bits
+            vb[b, :, n:] = nan_bits
+    return qb, kb, vb, lengths
+
+
+def run_gpu_decode(w, qb, kb, vb, lengths, tau, export=True, stats=True):
+    import torch
+
+    import block_sparse_flashattention_amd as bsfa
+
+    dev = torch.device("cuda")
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    lens = torch.tensor(np.asarray(lengths, dtype=np.int32), device=dev)
+    out_dtype = torch.float32 if w.out_f32 else torch.bfloat16
+    out = torch.full((w.B, w.Hq, w.d), math.nan, dtype=out_dtype, device=dev)
+    tau_t = None if tau is None else torch.tensor(np.asarray(tau, dtype=np.float32), device=dev)
+    res = bsfa.decode(q, k, v, lens, mask=gpu_spec(w), tau=tau_t, out=out, stats=stats,
+                      export_tiles=export and tau is not None)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_tau_decode(w, quantile: float, seed: int = 1) -> np.ndarray:
+    qb, kb, _, lengths = inputs.generate_decode(w, seed)
+    return orc.calibrate_tau_decode(f64(qb), f64(kb), lengths, oracle_spec(w), quantile)
+
+
+def compare_decode(w, qb, kb, vb, lengths, res, tau, check_keep=True) -> Report:
+    """Compare one GPU decode result with the oracle: keep bits off the near-tau band,
+    block maxima, then O and LSE against the oracle run on the GPU's keep bits."""
+    spec = oracle_spec(w)
+    q, k, v = f64(qb), f64(kb), f64(vb)
+    tau_r = None if tau is None else np.asarray(tau, dtype=np.float64)
+    override = None
+    near_cnt, tmax_err, kept, total = 0, 0.0, 0, 0
+    ref = orc.decode(q, k, v, lengths, spec, tau=tau_r)
+    allowed = ref.allowed[:, None, :]
+    if tau is not None and res.keep is not None:
+        keep_gpu = res.keep.cpu().numpy().astype(bool)
+        tmax_gpu = res.tile_max.cpu().numpy().astype(np.float64)
+        # blocks that are not allowed export -inf and keep 0
+        assert np.all(np.isneginf(tmax_gpu[~np.broadcast_to(allowed, tmax_gpu.shape)]))
+        assert not keep_gpu[~np.broadcast_to(allowed, keep_gpu.shape)].any()
+        near = ((np.abs(ref.tile_max - tau_r[None, :, None]) <= NEAR_TAU) & allowed
+                & ~ref.forced[:, None, :])
+        near_cnt = int(near.sum())
+        if check_keep:
+            mism = (keep_gpu != ref.keep) & allowed & ~near
+            assert not mism.any(), f"keep bits differ on {int(mism.sum())} non-near blocks"
+        with np.errstate(invalid="ignore"):  # -inf - -inf where a block is not allowed
+            tmax_err = float(np.abs(np.where(allowed, tmax_gpu - ref.tile_max, 0.0)).max())
+        assert tmax_err <= NEAR_TAU, f"block maxima differ by {tmax_err}"
+        override = keep_gpu
+        kept = int((keep_gpu & allowed).sum())
+        total = int(np.broadcast_to(allowed, keep_gpu.shape).sum())
+        ref = orc.decode(q, k, v, lengths, spec, tau=tau_r, keep_override=override)
+    go = res.out.float().cpu().numpy()
+    gl = res.lse.cpu().numpy()
+    o_err = np.abs(go - ref.out).reshape(-1)
+    both_inf = np.isneginf(gl) & np.isneginf(ref.lse)
+    with np.errstate(invalid="ignore"):  # -inf - -inf on rows with no key
+        l_err = np.where(both_inf, 0.0, np.abs(gl - ref.lse)).reshape(-1)
+    rep = Report(float(o_err.max()), float(o_err.mean()), float(l_err.max()), near_cnt,
+                 kept, total, tmax_err)
+    log(f"{w.name} Lmax={w.Lmax} lengths={list(lengths)} Hq={w.Hq} Hkv={w.Hkv} d={w.d}: "
+        f"max|dO|={rep.o_max:.3e} mean|dO|={rep.o_mean:.3e} max|dLSE|={rep.lse_max:.3e} "
+        f"max|dM|={rep.tmax_err:.2e} near={near_cnt} kept={kept}/{total}")
+    assert np.isfinite(o_err).all(), "non-finite output"
+    assert rep.o_max <= O_MAX and rep.o_mean <= O_MEAN, rep
+    assert rep.lse_max <= LSE_MAX, rep
+    if res.stats is not None:
+        st = res.stats.cpu().numpy()
+        n_allowed = ref.allowed.sum(axis=1)[:, None]
+        assert np.array_equal(st[..., 0] + st[..., 1], np.broadcast_to(n_allowed, st[..., 0].shape))
+        if override is not None:
+            assert np.array_equal(st[..., 0], (override & allowed).sum(axis=2))
+    return rep

@@ -22,10 +22,11 @@ def test_library_exports_every_declared_symbol():
     lib = bsfa.load_library()
     names = _declared()
     assert set(names) >= {"bsfa_build_block_lists", "bsfa_fwd", "bsfa_skip_stats",
-                          "bsfa_last_error", "bsfa_abi_version"}
+                          "bsfa_last_error", "bsfa_abi_version", "bsfa_decode",
+                          "bsfa_decode_workspace_size"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.bsfa_abi_version() == 2
+    assert lib.bsfa_abi_version() == 3
 
 
 def test_two_call_sizing_and_too_small():
@@ -112,3 +113,63 @@ def test_skip_stats_argument_errors():
     lib = bsfa.load_library()
     assert lib.bsfa_skip_stats(None, 1, 1, 16, 16, None) == -1
     assert lib.bsfa_skip_stats(16, 1, 0, 16, 16, None) == -1
+
+
+def test_decode_workspace_size():
+    # B * Hq * ceil(ceil(max_len / 64) / 4) * (d + 4) * 4 bytes
+    assert bsfa.decode_workspace_size(4, 32, 65536, 128) == 4 * 32 * 256 * 132 * 4
+    assert bsfa.decode_workspace_size(1, 1, 1, 64) == 68 * 4
+    assert bsfa.decode_workspace_size(2, 3, 257, 64) == 2 * 3 * 2 * 68 * 4
+    assert bsfa.decode_workspace_size(0, 8, 100, 128) == 0
+    lib = bsfa.load_library()
+    nb = ctypes.c_int64(0)
+    assert lib.bsfa_decode_workspace_size(1, 1, 0, 128, ctypes.byref(nb)) == -1
+    assert lib.bsfa_decode_workspace_size(1, 1, 64, 96, ctypes.byref(nb)) == -2
+    assert lib.bsfa_decode_workspace_size(1, 1, 64, 128, None) == -1
+
+
+def _decode_call(lib, **kw):
+    args = dict(q=16, k=16, v=16, lengths=16, out=16, lse=None, B=2, Hq=8, Hkv=2, L=1024,
+                d=128, mask=binding._CMask(1, 0, 0, 1, 1), tau=None, scale=0.0, out_dtype=0,
+                stats=None, tile_max=None, keep=None, ws=16, ws_bytes=1 << 30)
+    skn = kw.pop("skn", 128)
+    args.update(kw)
+    sq = binding._CStrides(8 * 128, 128, 0)
+    sk = binding._CStrides(2 * 1024 * 128, 1024 * 128, skn)
+    return lib.bsfa_decode(args["q"], args["k"], args["v"], args["lengths"], args["out"],
+                           args["lse"], args["B"], args["Hq"], args["Hkv"], args["L"],
+                           args["d"], ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sk),
+                           ctypes.byref(sq),
+                           ctypes.byref(args["mask"]) if args["mask"] is not None else None,
+                           args["tau"], args["scale"], args["out_dtype"], args["stats"],
+                           args["tile_max"], args["keep"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=7), -1),                         # Hq not a multiple of Hkv
+    (dict(Hq=66, Hkv=2), -2),                 # more than 32 query heads per KV head
+    (dict(d=96), -2),
+    (dict(L=0), -1),
+    (dict(mask=None), -1),
+    (dict(out_dtype=5), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(keep=16), -1),                      # keep without tile_max
+    (dict(tile_max=16, keep=16), -1),         # export without tau
+    (dict(lengths=None), -1),
+    (dict(ws=None), -1),
+    (dict(ws=8), -2),                         # misaligned workspace
+    (dict(lengths=18), -2),                   # misaligned lengths
+    (dict(ws_bytes=1000), -3),                # workspace too small
+    (dict(skn=-128), -2),
+    (dict(skn=1 << 21), -2),                  # one head's cache rows span 2^31 bytes or more
+])
+def test_decode_argument_errors(kw, code):
+    lib = bsfa.load_library()
+    assert _decode_call(lib, **kw) == code
+    assert lib.bsfa_last_error() != b""
+
+
+def test_decode_empty_batch_is_a_no_op():
+    lib = bsfa.load_library()
+    assert _decode_call(lib, B=0, q=None, out=None) == 0
+    assert lib.bsfa_last_error() == b""
