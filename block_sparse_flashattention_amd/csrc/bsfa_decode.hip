@@ -332,83 +332,77 @@ __global__ __launch_bounds__(128) void bsfa_decode_kernel(const DecArgs a) {
   }
 }
 
-// Merge the splits of one (sequence, query head). Four waves; wave w takes splits
-// w, w + 4, ... and every lane keeps several independent loads in flight; the partial
-// sums meet in LDS.
-constexpr int COMBINE_WAVES = 4;
+// Merge the splits of one (sequence, query head) for 32 of its d outputs: each
+// workgroup is one (sequence, head, 32-wide slice of d). Eight groups of 32 lanes take
+// interleaved splits, each lane one output element, with several independent loads in
+// flight; the group sums meet in LDS.
+constexpr int COMBINE_THREADS = 256;
+constexpr int COMBINE_GROUPS = COMBINE_THREADS / 32;
 
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(64 * COMBINE_WAVES) void bsfa_decode_combine(const DecArgs a) {
+__global__ __launch_bounds__(COMBINE_THREADS) void bsfa_decode_combine(const DecArgs a) {
   constexpr int WSR = D + WS_ROW_PAD;
-  constexpr int PER = D / 64;  // output elements per lane
-  constexpr int UNROLL = 4;
-  __shared__ float sRed[COMBINE_WAVES][D + 1];
-  __shared__ float sMx[COMBINE_WAVES];
+  constexpr int SLICES = D / 32;
+  constexpr int UNROLL = 16;
+  __shared__ float sAcc[COMBINE_GROUPS][33];
+  __shared__ float sMx[COMBINE_THREADS / 64];
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int64_t bh = blockIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = tid >> 5, el = tid & 31;
+  const int64_t bh = blockIdx.x / SLICES;
+  const int slice = blockIdx.x % SLICES;
   const int b = (int)(bh / a.Hq), h = (int)(bh % a.Hq);
+  const int d = slice * 32 + el;
   const float* base = a.ws + bh * a.nsplit * WSR;
 
   // the largest split LSE
   float mx = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += 64 * COMBINE_WAVES)
+  for (int s = tid; s < a.nsplit; s += COMBINE_THREADS)
     mx = fmaxf(mx, base[(int64_t)s * WSR + D]);
   mx = wave_max(mx);
   if (lane == 0) sMx[wave] = mx;
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < COMBINE_WAVES; ++w) mx = fmaxf(mx, sMx[w]);
+  for (int w = 0; w < COMBINE_THREADS / 64; ++w) mx = fmaxf(mx, sMx[w]);
 
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  float tot = 0.0f;
+  float acc = 0.0f, tot = 0.0f;
   if (mx != -INFINITY) {
-    for (int s0 = wave; s0 < a.nsplit; s0 += COMBINE_WAVES * UNROLL) {
-      float ls[UNROLL], vals[UNROLL][PER];
+    for (int s0 = grp; s0 < a.nsplit; s0 += COMBINE_GROUPS * UNROLL) {
+      float ls[UNROLL], val[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int s = s0 + u * COMBINE_WAVES;
+        const int s = s0 + u * COMBINE_GROUPS;
         const bool ok = s < a.nsplit;
         const float* row = base + (int64_t)(ok ? s : 0) * WSR;
         ls[u] = ok ? row[D] : -INFINITY;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) vals[u][e] = row[lane + 64 * e];
+        val[u] = row[d];
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         // a split with no kept key has LSE -inf and weight 0 (its O_s row is 0 too)
         const float wgt = ls[u] == -INFINITY ? 0.0f : expf(ls[u] - mx);
         tot += wgt;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, vals[u][e], acc[e]);
+        acc = fmaf(wgt, val[u], acc);
       }
     }
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) sRed[wave][lane + 64 * e] = acc[e];
-  if (lane == 0) sRed[wave][D] = tot;
+  sAcc[grp][el] = acc;
+  if (el == 0) sAcc[grp][32] = tot;
   __syncthreads();
-  if (wave == 0) {
-    float t = 0.0f;
+  if (tid < 32) {
+    float v = 0.0f, t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < COMBINE_WAVES; ++w) t += sRed[w][D];
-    const float inv = t > 0.0f ? 1.0f / t : 0.0f;
-    const int64_t obase = (int64_t)b * a.sob + (int64_t)h * a.soh;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      float v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < COMBINE_WAVES; ++w) v += sRed[w][lane + 64 * e];
-      const float val = v * inv;
-      if constexpr (OUT_F32)
-        reinterpret_cast<float*>(a.out)[obase + lane + 64 * e] = val;
-      else
-        reinterpret_cast<__bf16*>(a.out)[obase + lane + 64 * e] = (__bf16)val;
+    for (int g = 0; g < COMBINE_GROUPS; ++g) {
+      v += sAcc[g][el];
+      t += sAcc[g][32];
     }
-    if (a.lse && lane == 0) a.lse[bh] = t > 0.0f ? mx + logf(t) : -INFINITY;
+    const float val = t > 0.0f ? v / t : 0.0f;
+    const int64_t o = (int64_t)b * a.sob + (int64_t)h * a.soh + d;
+    if constexpr (OUT_F32)
+      reinterpret_cast<float*>(a.out)[o] = val;
+    else
+      reinterpret_cast<__bf16*>(a.out)[o] = (__bf16)val;
+    if (a.lse && slice == 0 && el == 0) a.lse[bh] = t > 0.0f ? mx + logf(t) : -INFINITY;
   }
 }
 
@@ -429,8 +423,8 @@ hipError_t launch_decode_d(const DecArgs& a, bool out_f32, hipStream_t s) {
   else
     e = launch_split<D, DEC_GATED>(a, s);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((int64_t)a.B * a.Hq);
-  const dim3 block(64 * COMBINE_WAVES);
+  const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * (D / 32));
+  const dim3 block(COMBINE_THREADS);
   if (out_f32)
     hipLaunchKernelGGL((bsfa_decode_combine<D, true>), dim3(grid), block, 0, s, a);
   else

@@ -416,7 +416,7 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (workspace_bytes < need)
     return fail(BSFA_ERR_BUFFER_TOO_SMALL, "workspace %lld bytes < %lld",
                 (long long)workspace_bytes, (long long)need);
-  if ((int64_t)B * Hkv * nsplit > INT32_MAX || (int64_t)B * Hq > INT32_MAX)
+  if ((int64_t)B * Hkv * nsplit > INT32_MAX || (int64_t)B * Hq * (d / 32) > INT32_MAX)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
 
   bsfa::DecArgs a;
