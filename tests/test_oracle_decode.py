@@ -3,8 +3,9 @@ key/value cache; "SAS: Sparse Attention Synthesizer", Challenge 2 "KV Cache Mana
 and Step 6; the gate of "Block Sparse Flash Attention", "The paper's summary").
 
 The dense path is pinned to torch's fp64 scaled_dot_product_attention over the cached
-rows; the gate to closed forms (Q = 0, tau = +inf) and to plain loops over the
-definitions; lengths to their edge cases.
+rows; the gate to closed forms (Q = 0, tau = +inf, a window-cut block whose masked keys
+would pass the gate) and to plain loops over the definitions; lengths to their edge
+cases.
 """
 import math
 
@@ -175,3 +176,24 @@ def test_calibration_hits_target_and_monotone_keep():
         assert abs(skipped - eligible.sum() / 2) <= 1
     lo = orc.decode(q, k, v, lengths, spec, tau=taus - 0.3)
     assert np.all(lo.keep >= r.keep)
+
+
+def test_gate_ignores_statically_masked_keys():
+    """Closed form: in the block that the window cuts, the keys outside the window score
+    high and the keys inside score low, with tau between them. The block's maximum is
+    taken over its allowed keys only, so it is skipped. Only the row's own block is kept,
+    and its keys all score 0, so O is the mean of their values and LSE = ln(count)."""
+    n, d, w = 200, 4, 50  # row 199 sees keys [150, 199]; block 2 holds 128..191
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 1.0
+    k = np.zeros((1, 1, n, d))
+    k[0, 0, 128:150, 0] = 40.0   # masked by the window, scaled scores 20
+    k[0, 0, 150:192, 0] = -4.0   # allowed, scaled scores -2
+    v = np.random.default_rng(3).standard_normal((1, 1, n, d))
+    spec = MaskSpec(causal=True, window=w)
+    r = orc.decode(q, k, v, [n], spec, tau=0.0)
+    assert r.allowed[0].tolist() == [False, False, True, True]
+    assert r.keep[0, 0].tolist() == [False, False, False, True]
+    np.testing.assert_allclose(r.out[0, 0], v[0, 0, 192:200].mean(0), atol=1e-12)
+    assert abs(r.lse[0, 0] - math.log(8)) < 1e-12
+    assert abs(r.tile_max[0, 0, 2] - (-2.0)) < 1e-12
