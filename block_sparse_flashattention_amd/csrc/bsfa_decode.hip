@@ -41,7 +41,11 @@ namespace {
 
 enum DecMode { DEC_DENSE = 0, DEC_GATED = 1, DEC_EXPORT = 2 };
 
-constexpr int WS_ROW_PAD = 4;  // workspace row: d values of O_s, LSE_s, padding to 16 B
+// Workspace: the rows O_s [B, Hq, nsplit, d], then LSE_s [B, Hq, nsplit] in one block,
+// so the combine reads each split's LSE from a compact array.
+__device__ __forceinline__ float* ws_lse(const DecArgs& a, int d) {
+  return a.ws + (int64_t)a.B * a.Hq * a.nsplit * d;
+}
 
 // SplitMix64 output for counter x (Steele, Lea and Flood, "Fast splittable pseudorandom
 // number generators", 2014).
@@ -97,7 +101,6 @@ __global__ __launch_bounds__(128) void bsfa_decode_kernel(const DecArgs a) {
   constexpr int DT = D / 32;  // 32-row tiles of O^T along d
   constexpr int KROW = D + 8;
   constexpr int VROW = D + 32;
-  constexpr int WSR = D + WS_ROW_PAD;
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[BLK * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[BLK * VROW];
@@ -314,7 +317,8 @@ __global__ __launch_bounds__(128) void bsfa_decode_kernel(const DecArgs a) {
     const float l = lw + sL[l32];
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (hv) {
-      float* wrow = a.ws + (((int64_t)b * a.Hq + hq) * a.nsplit + s) * WSR;
+      const int64_t part = ((int64_t)b * a.Hq + hq) * a.nsplit + s;
+      float* wrow = a.ws + part * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(128) void bsfa_decode_kernel(const DecArgs a) {
           v4.w = (o[dt][4 * r + 3] + sO[(dt * 16 + 4 * r + 3) * 64 + lane]) * inv;
           *reinterpret_cast<float4*>(wrow + d0) = v4;
         }
-      if (half == 0) wrow[D] = l > 0.0f ? m_h * a.scale + logf(l) : -INFINITY;
+      if (half == 0) ws_lse(a, D)[part] = l > 0.0f ? m_h * a.scale + logf(l) : -INFINITY;
     }
   }
 }
@@ -341,7 +345,6 @@ constexpr int COMBINE_GROUPS = COMBINE_THREADS / 32;
 
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(COMBINE_THREADS) void bsfa_decode_combine(const DecArgs a) {
-  constexpr int WSR = D + WS_ROW_PAD;
   constexpr int SLICES = D / 32;
   constexpr int UNROLL = 16;
   __shared__ float sAcc[COMBINE_GROUPS][33];
@@ -353,12 +356,12 @@ __global__ __launch_bounds__(COMBINE_THREADS) void bsfa_decode_combine(const Dec
   const int slice = blockIdx.x % SLICES;
   const int b = (int)(bh / a.Hq), h = (int)(bh % a.Hq);
   const int d = slice * 32 + el;
-  const float* base = a.ws + bh * a.nsplit * WSR;
+  const float* base = a.ws + bh * a.nsplit * D;
+  const float* lse_s = ws_lse(a, D) + bh * a.nsplit;
 
   // the largest split LSE
   float mx = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += COMBINE_THREADS)
-    mx = fmaxf(mx, base[(int64_t)s * WSR + D]);
+  for (int s = tid; s < a.nsplit; s += COMBINE_THREADS) mx = fmaxf(mx, lse_s[s]);
   mx = wave_max(mx);
   if (lane == 0) sMx[wave] = mx;
   __syncthreads();
@@ -373,9 +376,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void bsfa_decode_combine(const Dec
       for (int u = 0; u < UNROLL; ++u) {
         const int s = s0 + u * COMBINE_GROUPS;
         const bool ok = s < a.nsplit;
-        const float* row = base + (int64_t)(ok ? s : 0) * WSR;
-        ls[u] = ok ? row[D] : -INFINITY;
-        val[u] = row[d];
+        ls[u] = ok ? lse_s[s] : -INFINITY;
+        val[u] = base[(int64_t)(ok ? s : 0) * D + d];
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
