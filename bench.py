@@ -52,15 +52,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel source; else None."""
+def _record_matches(rec, workload, quantile):
+    return rec.get("workload_name") == workload and rec.get("tau_quantile") == quantile
+
+
+def measured_traffic(workload, quantile):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this
+    workload and tau quantile and on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if not _record_matches(rec, workload, quantile):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -71,9 +77,10 @@ DECODE_SOURCES = [os.path.join(ROOT, "block_sparse_flashattention_amd", "csrc", 
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsfa_decode_sink_local_64k_traffic.json")
 
 
-def measured_decode_traffic():
+def measured_decode_traffic(workload, quantile):
     """HBM bytes per decode step (both kernels) from the committed counter summary, if it
-    was taken on the current decode source; else None."""
+    was taken on this workload and tau quantile and on the current decode source; else
+    None."""
     try:
         with open(DECODE_TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -84,6 +91,8 @@ def measured_decode_traffic():
         with open(p, "rb") as f:
             h.update(f.read())
     if rec.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    if not _record_matches(rec, workload, quantile):
         return None
     return rec.get("hbm_bytes_per_step")
 
@@ -311,7 +320,7 @@ def bench_decode(args, w):
                    "tau_quantile": args.quantile, "block": "1x64"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_decode_traffic()},
+                     "traffic": measured_decode_traffic(w.name, args.quantile)},
         "tokens_per_s": round(w.B / (gated_ms / 1e3), 1),
         "dense_path_ms": round(dense_ms, 5),
         "dense_path_gbs": round(dense_bytes / (dense_kern / 1e3) / 1e9, 1),
@@ -481,7 +490,7 @@ def main():
                    "out_dtype": "f32" if w.out_f32 else "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(w.name, args.quantile)},
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(dense_flop / (head["ms"] / 1e3) / 1e12, 2),
         "dense_path_ms": round(dense_ms, 4),
