@@ -24,7 +24,7 @@ Sources (web pages this project is built from; cited by page title and section):
   are visible to every token. "SAS: Sparse Attention Synthesizer", Step 5 (Logic
   Operators): static primitives are combined with OR.
 
-Readings taken where the pages leave a step open (each is also listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * Skipped blocks leave both the softmax numerator and its denominator: the weights of
   the kept keys are renormalised to sum to one (as the worked example's weights do).
@@ -372,7 +372,7 @@ def calibrate_tau(
 # The pages describe token generation as one new token at a time over a cache of the
 # keys and values of all earlier tokens ("SAS: Sparse Attention Synthesizer", Challenge 2
 # "KV Cache Management" and Step 6), and the block gate for prefill ("Block Sparse Flash
-# Attention", "The paper's summary"). Reading taken for decode (listed in the design doc):
+# Attention", "The paper's summary"). Reading taken for decode:
 # the query tile is that single row. Each 64-key block of the cache gets the maximum of
 # the row's scaled scores over its allowed keys. The block is kept when forced (it holds
 # the row's own key, or a global key) or when that maximum is >= tau_h. The output is

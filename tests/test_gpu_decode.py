@@ -31,6 +31,7 @@ SHAPES = [
     DW("dec_g8_planted", 2, 16, 2, 2048, 128, lengths=(2048, 1999), kind="planted",
        planted_frac=0.1),
     DW("dec_g32", 1, 32, 1, 1200, 128, lengths=(1111,), kind="sink_local"),
+    DW("dec_g4_d64", 2, 8, 2, 900, 64, lengths=(900, 333), kind="planted", planted_frac=0.1),
 ]
 
 

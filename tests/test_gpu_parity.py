@@ -59,6 +59,7 @@ def test_static_mask_4k_dense_and_gated_minus_inf():
     (1000, 4, 2, 128, True, 0, 0, "planted"),       # ragged tail, 2 heads per workgroup
     (200, 2, 2, 64, False, 90, 7, "gaussian"),      # ragged, non-causal window + globals
     (640, 8, 2, 128, True, 0, 0, "planted"),        # 4 heads per workgroup
+    (520, 8, 2, 64, False, 150, 9, "gaussian"),     # 4 heads per workgroup at d = 64, ragged
     (777, 3, 1, 64, True, 130, 64, "gaussian"),     # 3 query heads share one KV head
     (64, 1, 1, 128, True, 0, 0, "gaussian"),        # a single tile
     (1, 1, 1, 64, True, 0, 0, "gaussian"),          # a single token
@@ -74,6 +75,12 @@ def test_batch_and_fp32_output():
     w = inputs.Workload("batch2", 2, 4, 1, 384, 128, causal=True, kind="planted",
                         planted_frac=0.2, out_f32=True)
     _case(w, tau_quantile=0.6)
+
+
+def test_four_heads_d64_fp32_output():
+    w = inputs.Workload("d64_pack4", 1, 8, 2, 1100, 64, causal=True, kind="planted",
+                        planted_frac=0.15, out_f32=True)
+    _case(w, tau_quantile=0.5)
 
 
 def test_tau_nan_and_plus_inf_keep_only_forced():
