@@ -173,3 +173,18 @@ def test_decode_empty_batch_is_a_no_op():
     lib = bsfa.load_library()
     assert _decode_call(lib, B=0, q=None, out=None) == 0
     assert lib.bsfa_last_error() == b""
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises: there is no CPU path."""
+    import torch
+
+    monkeypatch.setattr(binding, "_LIB", None)
+    monkeypatch.setattr(binding, "library_path", lambda: str(tmp_path / "libbsfa.so"))
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(binding.BsfaError, match="missing"):
+        bsfa.fwd(x, x, x, mask=bsfa.MaskSpec(causal=True))
+    with pytest.raises(binding.BsfaError, match="missing"):
+        bsfa.decode(x[:, :, 0], x, x, torch.tensor([64]), mask=bsfa.MaskSpec(causal=True))
+    with pytest.raises(binding.BsfaError, match="missing"):
+        binding.build_block_lists(bsfa.MaskSpec(causal=True), 64)
