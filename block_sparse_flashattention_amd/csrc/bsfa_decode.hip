@@ -93,10 +93,10 @@ __device__ __forceinline__ uint64_t row_mask(const DecArgs& a, int n, int i, int
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(128) void bsfa_decode_kernel(const DecArgs a) {
+__global__ __launch_bounds__(DEC_SPLIT_THREADS) void bsfa_decode_kernel(const DecArgs a) {
   constexpr bool GATE = MODE != DEC_DENSE;
   constexpr bool EXPORT = MODE == DEC_EXPORT;
-  constexpr int NT = 128;
+  constexpr int NT = DEC_SPLIT_THREADS;
   constexpr int KS = D / 16;  // 16-wide d steps of S^T = K Q^T
   constexpr int DT = D / 32;  // 32-row tiles of O^T along d
   constexpr int KROW = D + 8;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(128) void bsfa_decode_kernel(const DecArgs a) {
 // workgroup is one (sequence, head, 32-wide slice of d). Eight groups of 32 lanes take
 // interleaved splits, each lane one output element, with several independent loads in
 // flight; the group sums meet in LDS.
-constexpr int COMBINE_THREADS = 256;
+constexpr int COMBINE_THREADS = DEC_COMBINE_THREADS;
 constexpr int COMBINE_GROUPS = COMBINE_THREADS / 32;
 
 template <int D, bool OUT_F32>
@@ -411,7 +411,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void bsfa_decode_combine(const Dec
 template <int D, int MODE>
 hipError_t launch_split(const DecArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.nsplit);
-  hipLaunchKernelGGL((bsfa_decode_kernel<D, MODE>), dim3(grid), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((bsfa_decode_kernel<D, MODE>), dim3(grid), dim3(DEC_SPLIT_THREADS), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

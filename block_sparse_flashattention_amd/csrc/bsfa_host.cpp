@@ -319,7 +319,10 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   const int group = Hq / Hkv;
   const int hpack = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
   const int64_t grid = (int64_t)B * (Hq / hpack) * nqt;
-  if (grid > INT32_MAX) return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+  // one dispatch counts its work-items in 32 bits
+  const int64_t wg_threads = hpack == 4 ? 512 : 128 * hpack;
+  if (grid * wg_threads > (int64_t)UINT32_MAX)
+    return fail(BSFA_ERR_UNSUPPORTED, "grid of %lld workgroups too large", (long long)grid);
 
   bsfa::FwdArgs a;
   memset(&a, 0, sizeof a);
@@ -416,7 +419,9 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (workspace_bytes < need)
     return fail(BSFA_ERR_BUFFER_TOO_SMALL, "workspace %lld bytes < %lld",
                 (long long)workspace_bytes, (long long)need);
-  if ((int64_t)B * Hkv * nsplit > INT32_MAX || (int64_t)B * Hq * (d / 32) > INT32_MAX)
+  // one dispatch counts its work-items in 32 bits
+  if ((int64_t)B * Hkv * nsplit * bsfa::DEC_SPLIT_THREADS > (int64_t)UINT32_MAX ||
+      (int64_t)B * Hq * (d / 32) * bsfa::DEC_COMBINE_THREADS > (int64_t)UINT32_MAX)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
 
   bsfa::DecArgs a;

@@ -40,6 +40,8 @@ struct FwdArgs {
 // Everything one decode launch needs: one new query row per (sequence, query head)
 // against a key/value cache, in splits of DEC_BPS key blocks per workgroup.
 constexpr int DEC_BPS = 4;  // 64-key blocks per split (one workgroup)
+constexpr int DEC_SPLIT_THREADS = 128;    // threads per split workgroup
+constexpr int DEC_COMBINE_THREADS = 256;  // threads per combine workgroup
 
 struct DecArgs {
   const uint16_t* q;        // bf16 bits [B, Hq, d]

@@ -95,6 +95,7 @@ def _fwd_call(lib, **kw):
     (dict(B=-1), -1),
     (dict(sqn=-128), -2),                     # negative stride
     (dict(skn=1 << 24), -2),                  # one head's K/V rows span more than 2^31 bytes
+    (dict(B=1 << 23), -2),                    # more than 2^32 work-items in one dispatch
 ])
 def test_fwd_argument_errors(kw, code):
     lib = bsfa.load_library()
@@ -162,6 +163,7 @@ def _decode_call(lib, **kw):
     (dict(ws_bytes=1000), -3),                # workspace too small
     (dict(skn=-128), -2),
     (dict(skn=1 << 21), -2),                  # one head's cache rows span 2^31 bytes or more
+    (dict(B=1 << 22, ws_bytes=1 << 40), -2),  # more than 2^32 work-items in one dispatch
 ])
 def test_decode_argument_errors(kw, code):
     lib = bsfa.load_library()
