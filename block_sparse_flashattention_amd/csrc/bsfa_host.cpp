@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <new>
 #include <string>
 
 #include "../../include/bsfa.h"
@@ -475,7 +476,9 @@ int bsfa_skip_stats(const uint64_t* stats_dev, int32_t B, int32_t Hq, uint64_t* 
   if (B < 0 || Hq < 1) return fail(BSFA_ERR_INVALID_ARG, "need B >= 0 and Hq >= 1");
   const size_t n = (size_t)B * (size_t)Hq;
   if (n == 0) return ok();
-  uint64_t* both = new uint64_t[2 * n];
+  // no exception may cross the C ABI: a failed host allocation is an error code
+  uint64_t* both = new (std::nothrow) uint64_t[2 * n];
+  if (!both) return fail(BSFA_ERR_INVALID_ARG, "cannot allocate %zu host bytes", 2 * n * 8);
   const char* err = nullptr;
   const int rc = bsfa::copy_to_host_sync(both, stats_dev, 2 * n * sizeof(uint64_t), stream, &err);
   if (rc == BSFA_OK) {
