@@ -184,6 +184,25 @@ class FwdResult:
     lists: BlockLists = None
 
 
+def _on_device(dev, **tensors):
+    """Every tensor the kernels touch must live on the GPU that runs them: a host or
+    foreign-device pointer would reach the kernel as an invalid address."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise BsfaError(-1, f"{name} is on {t.device}, the call runs on {dev}")
+
+
+def _buffer(name, t, shape, dtypes, contiguous=True):
+    """A caller-provided output buffer: exact shape, dtype, and (if the kernel indexes it
+    densely) contiguous."""
+    if tuple(t.shape) != tuple(shape):
+        raise BsfaError(-1, f"{name} has shape {tuple(t.shape)}, need {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise BsfaError(-2, f"{name} has dtype {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise BsfaError(-2, f"{name} must be contiguous")
+
+
 def _strides(t) -> _CStrides:
     s = t.stride()
     if s[3] != 1:
@@ -215,16 +234,22 @@ def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0
     if tuple(k.shape) != (bsz, hkv, n, d) or tuple(v.shape) != (bsz, hkv, n, d):
         raise BsfaError(-1, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     dev = q.device
+    _on_device(dev, q=q, k=k, v=v, out=out, lse_out=lse_out, stats_out=stats_out)
     if out_dtype is None:
         out_dtype = torch.bfloat16
     if out is None:
         out = torch.empty((bsz, hq, n, d), dtype=out_dtype, device=dev)
+    _buffer("out", out, (bsz, hq, n, d), (torch.bfloat16, torch.float32), contiguous=False)
     if lse_out is not None:
+        _buffer("lse_out", lse_out, (bsz, hq, n), (torch.float32,))
         lse = lse_out
     else:
         lse = torch.empty((bsz, hq, n), dtype=torch.float32, device=dev) if want_lse else None
+    if stats_out is not None:
+        _buffer("stats_out", stats_out, (bsz, hq, 2), (torch.int64,))
     if lists is None:
         lists = BlockLists.get(mask, n, dev)
+    _on_device(dev, lists=lists.row_ptr)
     tau_t = None
     if tau is not None:
         tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
@@ -309,16 +334,22 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
     if q.stride(2) != 1:
         raise BsfaError(-2, "the head dimension of q must be contiguous")
     dev = q.device
+    _on_device(dev, q=q, k_cache=k_cache, v_cache=v_cache, lengths=lengths, out=out,
+               lse_out=lse_out, stats_out=stats_out, workspace=workspace)
     if out_dtype is None:
         out_dtype = torch.bfloat16
     if out is None:
         out = torch.empty((bsz, hq, d), dtype=out_dtype, device=dev)
+    _buffer("out", out, (bsz, hq, d), (torch.bfloat16, torch.float32), contiguous=False)
     if out.stride(2) != 1:
         raise BsfaError(-2, "the head dimension of out must be contiguous")
     if lse_out is not None:
+        _buffer("lse_out", lse_out, (bsz, hq), (torch.float32,))
         lse = lse_out
     else:
         lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if want_lse else None
+    if stats_out is not None:
+        _buffer("stats_out", stats_out, (bsz, hq, 2), (torch.int64,))
     tau_t = None
     if tau is not None:
         tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
@@ -339,6 +370,8 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
     need = decode_workspace_size(bsz, hq, lmax, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif not workspace.is_contiguous():
+        raise BsfaError(-2, "workspace must be contiguous")
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     cm = mask._c()
@@ -395,7 +428,10 @@ def skip_stats(stats_tensor, stream=None):
     import torch
 
     lib = load_library()
+    if not stats_tensor.is_cuda:
+        raise BsfaError(-1, "stats_tensor must be on the GPU")
     bsz, hq, _ = stats_tensor.shape
+    _buffer("stats_tensor", stats_tensor, (bsz, hq, 2), (torch.int64,))
     kept = np.zeros((bsz, hq), dtype=np.uint64)
     skipped = np.zeros((bsz, hq), dtype=np.uint64)
     if stream is None:

@@ -190,3 +190,32 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         bsfa.decode(x[:, :, 0], x, x, torch.tensor([64]), mask=bsfa.MaskSpec(causal=True))
     with pytest.raises(binding.BsfaError, match="missing"):
         binding.build_block_lists(bsfa.MaskSpec(causal=True), 64)
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    """Tensors that are not on the GPU never reach the library: their pointers would be
+    invalid device addresses."""
+    import torch
+
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(binding.BsfaError, match="is on cpu"):
+        bsfa.fwd(x, x, x, mask=bsfa.MaskSpec(causal=True))
+    with pytest.raises(binding.BsfaError, match="is on cpu"):
+        bsfa.decode(x[:, :, 0], x, x, torch.tensor([64], dtype=torch.int32),
+                    mask=bsfa.MaskSpec(causal=True))
+    with pytest.raises(binding.BsfaError, match="on the GPU"):
+        binding.skip_stats(torch.zeros((1, 1, 2), dtype=torch.int64))
+
+
+def test_buffer_checks():
+    import torch
+
+    t = torch.zeros((2, 3, 5), dtype=torch.float32)
+    binding._buffer("lse_out", t, (2, 3, 5), (torch.float32,))
+    with pytest.raises(binding.BsfaError, match="shape"):
+        binding._buffer("lse_out", t, (2, 3, 6), (torch.float32,))
+    with pytest.raises(binding.BsfaError, match="dtype"):
+        binding._buffer("lse_out", t, (2, 3, 5), (torch.int64,))
+    with pytest.raises(binding.BsfaError, match="contiguous"):
+        binding._buffer("lse_out", t.transpose(0, 2).contiguous().transpose(0, 2),
+                        (2, 3, 5), (torch.float32,))
