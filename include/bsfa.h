@@ -156,7 +156,8 @@ int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_
  *   stream  : hipStream_t (NULL = default stream). The call is asynchronous.
  * Pointers q, k, v, out must be 16-byte aligned and the n/h/b strides non-negative
  * multiples of 8. The K (and V) rows of one (batch, KV head), ((N - 1) * n-stride + d)
- * elements, must span fewer than 2^31 bytes; otherwise BSFA_ERR_UNSUPPORTED.
+ * elements, must span fewer than 2^31 bytes; otherwise BSFA_ERR_UNSUPPORTED. So is a
+ * launch of 2^32 or more work-items: B * Hq * ceil(N / 64) * 128 must stay below 2^32.
  */
 int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
@@ -218,7 +219,9 @@ int bsfa_decode_workspace_size(int32_t B, int32_t Hq, int32_t max_len, int32_t d
  * Pointers q, k_cache, v_cache, out must be 16-byte aligned and the used strides
  * non-negative multiples of 8; the cache rows of one (sequence, KV head),
  * ((max_len - 1) * n-stride + d) elements, must span fewer than 2^31 bytes.
- * Errors: BSFA_ERR_BUFFER_TOO_SMALL for a short workspace, otherwise as bsfa_fwd.
+ * Errors: BSFA_ERR_BUFFER_TOO_SMALL for a short workspace, otherwise as bsfa_fwd; the
+ * work-item limit applies to B * Hkv * ceil(ceil(max_len / 64) / 4) * 128 and to
+ * B * Hq * (d / 32) * 256.
  */
 int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
