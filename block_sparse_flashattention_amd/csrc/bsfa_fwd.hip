@@ -731,7 +731,10 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
       for (int rh = 0; rh < 2; ++rh)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) sn[rh][mt] = f32x16_t{};
-      constexpr int PF = 2;  // K fragments read ahead
+      // K fragments read ahead. A skipped step (QK^T and the maximum only) reads 4 ahead
+      // and pins each read in place: left free, the scheduler moved the reads next to
+      // their MFMAs and waited out every read's latency.
+      constexpr int PF = KEEP ? 2 : 4;
       bf16x8_t kf[PF];
       auto fr = [](int n) { return 2 * (n % KS) + n / KS; };  // key half outer
 #pragma unroll
@@ -741,6 +744,7 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
       for (int n = 0; n < NKF; ++n) {
         const bf16x8_t kcur = kf[n % PF];
         if (n + PF < NKF) kf[n % PF] = k_frag(kt, fr(n + PF));
+        if constexpr (!KEEP) __builtin_amdgcn_sched_barrier(0);
         const int f = fr(n), mt = f & 1, ks = f >> 1;
         sn[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[0][ks], sn[0][mt], 0, 0, 0);
         sn[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[1][ks], sn[1][mt], 0, 0, 0);
