@@ -90,3 +90,29 @@ def test_long_sequence_counts():
         bsfa.MaskSpec(causal=True, window=1024, n_global=64), 4096)
     _check(dict(causal=True, window=1024, n_global=64), 4096, 64, 64)
     assert col.size == 999
+
+
+def test_concurrent_host_calls_agree():
+    """bsfa_build_block_lists and the error text are per-call / per-thread: eight threads
+    building different lists at once (half of them failing on purpose) each get the lists
+    or the error that a serial call gives."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from block_sparse_flashattention_amd import binding
+
+    specs = [bsfa.MaskSpec(causal=True, window=w, n_global=g) for w in (0, 300) for g in (0, 70)]
+    sizes = [1000, 4097]
+    jobs = [(s, n) for s in specs for n in sizes]
+    serial = [binding.build_block_lists(s, n) for s, n in jobs]
+
+    def work(i):
+        if i % 2:  # an invalid call in between: its error must stay on this thread
+            with pytest.raises(binding.BsfaError):
+                binding.build_block_lists(bsfa.MaskSpec(causal=True, window=-1), 100)
+        return binding.build_block_lists(*jobs[i % len(jobs)])
+
+    with ThreadPoolExecutor(8) as ex:
+        got = list(ex.map(work, range(4 * len(jobs))))
+    for i, g in enumerate(got):
+        for a, b in zip(g, serial[i % len(jobs)]):
+            np.testing.assert_array_equal(a, b)
