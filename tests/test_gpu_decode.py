@@ -32,6 +32,7 @@ SHAPES = [
        planted_frac=0.1),
     DW("dec_g32", 1, 32, 1, 1200, 128, lengths=(1111,), kind="sink_local"),
     DW("dec_g4_d64", 2, 8, 2, 900, 64, lengths=(900, 333), kind="planted", planted_frac=0.1),
+    DW("dec_g8_d64", 2, 16, 2, 700, 64, lengths=(129, 700), kind="sink_local"),
 ]
 
 

@@ -60,6 +60,7 @@ def test_static_mask_4k_dense_and_gated_minus_inf():
     (200, 2, 2, 64, False, 90, 7, "gaussian"),      # ragged, non-causal window + globals
     (640, 8, 2, 128, True, 0, 0, "planted"),        # 4 heads per workgroup
     (520, 8, 2, 64, False, 150, 9, "gaussian"),     # 4 heads per workgroup at d = 64, ragged
+    (300, 8, 1, 128, False, 0, 0, "gaussian"),      # two packs share one KV head, no mask
     (777, 3, 1, 64, True, 130, 64, "gaussian"),     # 3 query heads share one KV head
     (64, 1, 1, 128, True, 0, 0, "gaussian"),        # a single tile
     (1, 1, 1, 64, True, 0, 0, "gaussian"),          # a single token
@@ -75,6 +76,14 @@ def test_batch_and_fp32_output():
     w = inputs.Workload("batch2", 2, 4, 1, 384, 128, causal=True, kind="planted",
                         planted_frac=0.2, out_f32=True)
     _case(w, tau_quantile=0.6)
+
+
+def test_batch_of_three_one_row_ragged_tail():
+    """Three sequences of N = 129: the last query tile and key block hold one row each."""
+    w = inputs.Workload("batch3_n129", 3, 8, 2, 129, 128, causal=True, kind="planted",
+                        planted_frac=0.3)
+    _case(w, tau_quantile=0.5)
+    _case(w, tau=None)
 
 
 def test_four_heads_d64_fp32_output():
