@@ -22,10 +22,11 @@
 //   query row (l32) and 32 of its 64 keys: key = 32*mt + 8*(i/4) + 4*h + i%4 for
 //   accumulator element i of key tile mt. The running max m and sum l are therefore
 //   per-lane scalars; a row reduction is a local loop plus one exchange with lane l^32.
-//   P^T then feeds the P.V MFMA (O^T = V^T P^T) as its B operand straight from the
-//   accumulator registers: for 16-key step ks the lane's 8 values are accumulator
-//   elements 8*(ks%2) .. +7 of tile ks/2. V^T rows come from a row-major V tile in LDS
-//   via ds_read_tr16_b64 (two 4-key reads per operand).
+//   P^T is the B operand of the P.V MFMA (O^T = V^T P^T): for 16-key step ks the lane's
+//   8 values are accumulator elements 8*(ks%2) .. +7 of tile ks/2. The lock-step kernel
+//   feeds them straight from the accumulator registers; the warp-specialised kernel
+//   writes them to LDS in that operand layout for the consumer wave. V^T rows come from
+//   a row-major V tile in LDS via ds_read_tr16_b64 (two 4-key reads per operand).
 //
 // The gate's tile maximum: local max over the lane's values, DPP all-reduce inside each
 // 16-lane row, readlane across rows. In the lock-step kernel it then goes through one LDS
@@ -46,9 +47,6 @@ namespace {
 
 #include "bsfa_device.h"
 
-// Keys j0 + k, k in [0, 64), that query row i may attend, as bit k of the result: each
-// static primitive (causal, N, window, dilated, blockwise, global tokens) is a range or
-// a residue class of k; `rnd` says the random primitive selects this 64 x 64 tile.
 // The fields of the further primitives, read when a partial tile needs them. They are
 // loaded from the kernel argument segment through an address the compiler cannot track,
 // so the loads stay on this rare path instead of holding scalar registers for the whole
@@ -73,6 +71,9 @@ __device__ __forceinline__ PatternArgs pattern_args() {
   return p;
 }
 
+// Keys j0 + k, k in [0, 64), that query row i may attend, as bit k of the result: each
+// static primitive (causal, N, window, dilated, blockwise, global tokens) is a range or
+// a residue class of k; `rnd` says the random primitive selects this 64 x 64 tile.
 __device__ __forceinline__ uint64_t row_mask(const FwdArgs& a, int i, int j0, bool rnd) {
   const PatternArgs pa = pattern_args();
   const int r = i - j0;  // k of the diagonal element (|r| < N < 2^31)
