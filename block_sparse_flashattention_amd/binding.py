@@ -7,6 +7,7 @@ missing or a call fails, a ``BsfaError`` is raised.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import math
 import os
@@ -148,7 +149,9 @@ def build_block_lists(mask: MaskSpec, n: int, block_q: int = 64, block_k: int = 
 class BlockLists:
     """Device copy of the 64x64 block lists for one (mask, N)."""
 
-    _cache: dict = {}
+    # the most recently used lists, by (mask, N, device); older ones are dropped
+    _cache: "collections.OrderedDict" = collections.OrderedDict()
+    CACHE_SIZE = 16
 
     def __init__(self, mask: MaskSpec, n: int, device):
         import torch
@@ -165,8 +168,12 @@ class BlockLists:
     @classmethod
     def get(cls, mask: MaskSpec, n: int, device) -> "BlockLists":
         key = (mask, n, str(device))
-        if key not in cls._cache:
+        if key in cls._cache:
+            cls._cache.move_to_end(key)
+        else:
             cls._cache[key] = cls(mask, n, device)
+            while len(cls._cache) > cls.CACHE_SIZE:
+                cls._cache.popitem(last=False)
         return cls._cache[key]
 
     def _c(self) -> _CLists:

@@ -219,3 +219,22 @@ def test_buffer_checks():
     with pytest.raises(binding.BsfaError, match="contiguous"):
         binding._buffer("lse_out", t.transpose(0, 2).contiguous().transpose(0, 2),
                         (2, 3, 5), (torch.float32,))
+
+
+def test_block_list_cache_is_bounded(monkeypatch):
+    """BlockLists.get keeps the most recently used lists only."""
+    calls = []
+
+    class Fake(binding.BlockLists):
+        _cache = __import__("collections").OrderedDict()
+        CACHE_SIZE = 3
+
+        def __init__(self, mask, n, device):
+            calls.append(n)
+
+    spec = bsfa.MaskSpec(causal=True)
+    for n in (64, 128, 192, 64, 256, 128):
+        Fake.get(spec, n, "cuda:0")
+    # 64 was reused before 256 evicted the oldest (128), so 128 is built again
+    assert calls == [64, 128, 192, 256, 128]
+    assert list(k[1] for k in Fake._cache) == [64, 256, 128]
