@@ -86,6 +86,17 @@ def test_batch_of_three_one_row_ragged_tail():
     _case(w, tau=None)
 
 
+def test_four_heads_d64_long_sampled():
+    """The four-head kernel at d = 64 over 128 query tiles, on sampled tiles of all heads."""
+    w = inputs.Workload("d64_pack4_8k", 1, 16, 4, 8192, 64, causal=True, window=3000,
+                        n_global=64, kind="planted", planted_frac=0.1)
+    nqt = w.N // 64
+    rng = np.random.default_rng(9)
+    tiles = sorted({0, 1, nqt - 1, *rng.choice(nqt, 3, replace=False).tolist()})
+    cal = sorted(rng.choice(nqt, 16, replace=False).tolist())
+    _case(w, tau_quantile=0.5, q_tiles=tiles, cal_tiles=cal)
+
+
 def test_four_heads_d64_fp32_output():
     w = inputs.Workload("d64_pack4", 1, 8, 2, 1100, 64, causal=True, kind="planted",
                         planted_frac=0.15, out_f32=True)
