@@ -26,6 +26,7 @@ _BINDING_NAMES = {
     "MaskSpec", "BlockLists", "BsfaError", "build_block_lists", "fwd", "skip_stats",
     "library_path", "load_library", "calibrate_tau", "calibration_maxima",
     "decode", "decode_workspace_size", "decode_calibrate_tau", "decode_calibration_maxima",
+    "gpu_quantiles", "calibrate_workspace_size",
 }
 
 

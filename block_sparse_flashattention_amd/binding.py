@@ -89,6 +89,12 @@ def load_library():
         ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.bsfa_decode.restype = ctypes.c_int
+    lib.bsfa_calibrate_workspace_size.argtypes = [ctypes.c_int32, P(ctypes.c_int64)]
+    lib.bsfa_calibrate_workspace_size.restype = ctypes.c_int
+    lib.bsfa_calibrate_tau.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.bsfa_calibrate_tau.restype = ctypes.c_int
     lib.bsfa_skip_stats.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.bsfa_skip_stats.restype = ctypes.c_int
@@ -421,13 +427,55 @@ def decode_calibration_maxima(q, k_cache, lengths, mask: MaskSpec, softmax_scale
 def decode_calibrate_tau(q, k_cache, lengths, mask: MaskSpec, quantile,
                          softmax_scale: float = 0.0, stream=None):
     """Per-head decode thresholds: the ``quantile`` of the eligible decode block maxima
-    of each query head on calibration inputs (as ``calibrate_tau`` for prefill)."""
-    maxima = decode_calibration_maxima(q, k_cache, lengths, mask, softmax_scale, stream)
+    of each query head on calibration inputs (as ``calibrate_tau`` for prefill). One
+    gate-only decode pass exports the maxima; ``bsfa_calibrate_tau`` takes the quantile
+    on the GPU."""
+    import torch
+
+    hq = q.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    res = decode(q, k_cache, k_cache, lengths, mask=mask,
+                 tau=torch.full((hq,), math.nan, device=q.device),
+                 softmax_scale=softmax_scale, want_lse=False, export_tiles=True,
+                 stream=stream)
+    nkb = -(-k_cache.shape[2] // 64)
+    return gpu_quantiles(res.tile_max, res.keep, q.shape[0], hq, nkb, quantile, stream)
+
+
+def calibrate_workspace_size(hq: int) -> int:
+    """Bytes of scratch ``gpu_quantiles`` needs (bsfa_calibrate_workspace_size)."""
+    lib = load_library()
+    nbytes = ctypes.c_int64(0)
+    _check(lib, lib.bsfa_calibrate_workspace_size(hq, ctypes.byref(nbytes)))
+    return int(nbytes.value)
+
+
+def gpu_quantiles(tile_max, keep, bsz: int, hq: int, n_blocks: int, quantile, stream=None):
+    """Per-head quantiles of the eligible exported block maxima, on the GPU
+    (bsfa_calibrate_tau): tile_max fp32 and keep uint8, both [B, Hq, n_blocks] on the
+    device. A scalar ``quantile`` returns fp32 [Hq]; a sequence returns fp32
+    [len(quantile), Hq]. Heads with no eligible block get -inf."""
+    import torch
+
+    lib = load_library()
+    dev = tile_max.device
+    _on_device(dev, tile_max=tile_max, keep=keep)
+    if n_blocks:
+        _buffer("tile_max", tile_max, (bsz, hq, n_blocks), (torch.float32,))
+        _buffer("keep", keep, (bsz, hq, n_blocks), (torch.uint8,))
     qs = np.atleast_1d(np.asarray(quantile, dtype=np.float64))
-    taus = np.empty((qs.size, len(maxima)), dtype=np.float32)
-    for h, vals in enumerate(maxima):
-        taus[:, h] = np.quantile(vals.astype(np.float64), qs) if vals.size else -np.inf
-    return taus[0] if np.ndim(quantile) == 0 else taus
+    taus = torch.empty((qs.size, hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(calibrate_workspace_size(hq), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    for i, qv in enumerate(qs):
+        _check(lib, lib.bsfa_calibrate_tau(tile_max.data_ptr(), keep.data_ptr(), bsz, hq,
+                                           n_blocks, float(qv), taus[i].data_ptr(),
+                                           ws.data_ptr(), ws.numel(), stream))
+    torch.cuda.synchronize(dev)  # the launches may sit on a stream other than torch's
+    out = taus.cpu().numpy()
+    return out[0] if np.ndim(quantile) == 0 else out
 
 
 def skip_stats(stats_tensor, stream=None):
@@ -475,11 +523,17 @@ def calibrate_tau(q, k, mask: MaskSpec, quantile, softmax_scale: float = 0.0, li
     paper's improvements": thresholds learned once per layer and head on a small data set).
 
     tau_h = the ``quantile`` of the eligible block maxima of query head h on calibration
-    inputs q, k (``calibration_maxima``). ``quantile`` may be a scalar (returns fp32
+    inputs q, k, with numpy's linear interpolation. One gate-only pass of the kernel
+    exports the maxima and ``bsfa_calibrate_tau`` takes the quantile on the GPU; nothing
+    is copied to the host but the result. ``quantile`` may be a scalar (returns fp32
     [Hq]) or a sequence (returns fp32 [len(quantile), Hq])."""
-    maxima = calibration_maxima(q, k, mask, softmax_scale, lists=lists, stream=stream)
-    qs = np.atleast_1d(np.asarray(quantile, dtype=np.float64))
-    taus = np.empty((qs.size, len(maxima)), dtype=np.float32)
-    for h, vals in enumerate(maxima):
-        taus[:, h] = np.quantile(vals.astype(np.float64), qs) if vals.size else -np.inf
-    return taus[0] if np.ndim(quantile) == 0 else taus
+    import torch
+
+    hq = q.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), math.nan, device=q.device),
+              softmax_scale=softmax_scale, want_lse=False, export_tiles=True, lists=lists,
+              stream=stream)
+    return gpu_quantiles(res.tile_max, res.keep, q.shape[0], hq, res.lists.nnz, quantile,
+                         stream)

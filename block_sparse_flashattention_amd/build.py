@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("bsfa_host.cpp", "bsfa_fwd.hip", "bsfa_decode.hip")]
+           for f in ("bsfa_host.cpp", "bsfa_fwd.hip", "bsfa_decode.hip", "bsfa_calib.hip")]
 OUTPUT = os.path.join(HERE, "libbsfa.so")
 
 # Packed fp32 VALU forms are disabled for all device code (-packed-fp32-ops); the host

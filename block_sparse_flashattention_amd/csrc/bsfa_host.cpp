@@ -197,6 +197,12 @@ bool view_fits(const bsfa_strides* s, int32_t N, int32_t d) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Calibration workspace: the per-head digit histograms, then the per-head select states.
+int64_t calib_workspace_bytes(int32_t Hq) {
+  return (int64_t)Hq * 256 * (int64_t)sizeof(uint32_t) +
+         (int64_t)Hq * (int64_t)sizeof(bsfa::CalibState);
+}
+
 // Decode splits: one workgroup per bsfa::DEC_BPS key blocks of the cache.
 int32_t decode_splits(int32_t max_len) {
   const int32_t nkb = (max_len + 63) / 64;
@@ -209,7 +215,7 @@ extern "C" {
 
 const char* bsfa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t bsfa_abi_version(void) { return 3; }
+int32_t bsfa_abi_version(void) { return 4; }
 
 int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_q,
                            int32_t block_k, int32_t* row_ptr, int32_t* col, uint8_t* cls,
@@ -465,6 +471,54 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.keep = keep;
   const char* err = nullptr;
   const int rc = bsfa::launch_decode(a, d, out_dtype == BSFA_OUT_F32, stream, &err);
+  if (rc != BSFA_OK) return fail(rc, "%s", err ? err : "launch failed");
+  return ok();
+}
+
+int bsfa_calibrate_workspace_size(int32_t Hq, int64_t* bytes) {
+  if (!bytes) return fail(BSFA_ERR_INVALID_ARG, "bytes is required");
+  if (Hq < 1) return fail(BSFA_ERR_INVALID_ARG, "need Hq >= 1");
+  *bytes = calib_workspace_bytes(Hq);
+  return ok();
+}
+
+int bsfa_calibrate_tau(const float* tile_max, const uint8_t* keep, int32_t B, int32_t Hq,
+                       int64_t n_blocks, double quantile, float* tau, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq < 1 || n_blocks < 0)
+    return fail(BSFA_ERR_INVALID_ARG, "need B >= 0, Hq >= 1, n_blocks >= 0");
+  if (!(quantile >= 0.0 && quantile <= 1.0))
+    return fail(BSFA_ERR_INVALID_ARG, "quantile must lie in [0, 1]");
+  if (!tau || !workspace) return fail(BSFA_ERR_INVALID_ARG, "tau and workspace are required");
+  const int64_t per_head = (int64_t)B * n_blocks;
+  if (per_head > 0 && (!tile_max || !keep))
+    return fail(BSFA_ERR_INVALID_ARG, "tile_max and keep are required");
+  if (per_head >= (int64_t)UINT32_MAX)
+    return fail(BSFA_ERR_UNSUPPORTED, "2^32 - 1 or more blocks per head");
+  const int64_t need = calib_workspace_bytes(Hq);
+  if (workspace_bytes < need)
+    return fail(BSFA_ERR_BUFFER_TOO_SMALL, "workspace %lld bytes < %lld",
+                (long long)workspace_bytes, (long long)need);
+  if (!aligned16(workspace) || ((uintptr_t)tile_max & 3u) || ((uintptr_t)tau & 3u))
+    return fail(BSFA_ERR_UNSUPPORTED,
+                "workspace must be 16-byte aligned, tile_max and tau 4-byte aligned");
+  // one dispatch counts its work-items in 32 bits
+  if (bsfa::calibrate_grid(B, Hq, n_blocks) * 256 > (int64_t)UINT32_MAX)
+    return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+  bsfa::CalibArgs a;
+  memset(&a, 0, sizeof a);
+  a.tile_max = tile_max;
+  a.keep = keep;
+  a.B = B;
+  a.Hq = Hq;
+  a.n_blocks = n_blocks;
+  a.q = quantile;
+  a.tau = tau;
+  a.hist = reinterpret_cast<uint32_t*>(workspace);
+  a.state = reinterpret_cast<bsfa::CalibState*>(reinterpret_cast<char*>(workspace) +
+                                                (int64_t)Hq * 256 * sizeof(uint32_t));
+  const char* err = nullptr;
+  const int rc = bsfa::launch_calibrate(a, stream, &err);
   if (rc != BSFA_OK) return fail(rc, "%s", err ? err : "launch failed");
   return ok();
 }

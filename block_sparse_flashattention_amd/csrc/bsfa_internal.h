@@ -75,6 +75,31 @@ struct DecArgs {
 // Launches the decode split kernel and the combine kernel on `stream`.
 int launch_decode(const DecArgs& a, int d, bool out_f32, void* stream, const char** err);
 
+// Per-head threshold calibration from exported block maxima (bsfa_calib.hip).
+struct CalibState {
+  uint32_t prefix, mask;  // selected high bits of the order statistic's key so far
+  uint32_t rank;          // wanted rank among the keys that match the prefix
+  uint32_t count_eq;      // how often the selected key occurs
+  uint32_t n, lo;         // eligible maxima; index of the lower order statistic
+  uint32_t minkey;        // smallest key above the selected one
+  uint32_t hi_same;       // both interpolation neighbours are the selected value
+  double vidx, prev;      // numpy's virtual index and adjusted previous index
+};
+
+struct CalibArgs {
+  const float* tile_max;   // [B, Hq, n_blocks] exported block maxima (scaled units)
+  const uint8_t* keep;     // [B, Hq, n_blocks] keep bits of the gate-only pass
+  int32_t B, Hq;
+  int64_t n_blocks;
+  double q;                // quantile in [0, 1]
+  float* tau;              // [Hq] result
+  uint32_t* hist;          // [Hq, 256] workspace
+  CalibState* state;       // [Hq] workspace
+};
+
+int launch_calibrate(const CalibArgs& a, void* stream, const char** err);
+int64_t calibrate_grid(int64_t B, int64_t Hq, int64_t n_blocks);
+
 // Launches the forward kernel variant for head dim d, head pack hpack (query heads of
 // one KV group sharing a workgroup), gated (tau != null) or dense, bf16 or fp32 output.
 // Returns 0 or a negative bsfa_status; *err receives a static message on failure.

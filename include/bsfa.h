@@ -232,6 +232,31 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Per-head threshold calibration on the GPU. Thresholds are learned once per layer and
+ * head from the distribution of block maxima on calibration data (Block Sparse Flash
+ * Attention, "The paper's improvements"); here tau_h is the `quantile` of head h's
+ * eligible block maxima with numpy's default linear interpolation, computed in fp64 and
+ * rounded to fp32. It equals np.quantile over the same maxima.
+ *   tile_max, keep: device fp32 / uint8 [B, Hq, n_blocks], the per-block export of one
+ *             gate-only pass (bsfa_fwd with tau = NaN and lists->nnz blocks per (b, h), or
+ *             bsfa_decode with tau = NaN and ceil(max_len / 64) blocks). A block is
+ *             eligible when keep is 0 (not forced) and its maximum is finite (allowed).
+ *   quantile: in [0, 1].
+ *   tau     : device fp32 [Hq], written; -inf for a head with no eligible block.
+ *   workspace, workspace_bytes: device scratch of at least
+ *             bsfa_calibrate_workspace_size(Hq) bytes, 16-byte aligned; its contents on
+ *             entry do not matter. Calls that share one workspace must not overlap.
+ *   stream  : hipStream_t; the call is asynchronous (ten small kernels).
+ * Errors: INVALID_ARG for negative sizes, a quantile outside [0, 1] or NaN, or missing
+ * pointers; BUFFER_TOO_SMALL for a short workspace; UNSUPPORTED for misaligned pointers,
+ * 2^32 - 1 or more blocks per head, or a dispatch of 2^32 or more work-items.
+ */
+int bsfa_calibrate_workspace_size(int32_t Hq, int64_t* bytes);
+int bsfa_calibrate_tau(const float* tile_max, const uint8_t* keep, int32_t B, int32_t Hq,
+                       int64_t n_blocks, double quantile, float* tau, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/*
  * Copy the per-(b, h) counters written by bsfa_fwd or bsfa_decode to the host and split
  * them.
  *   stats_dev: device uint64 [B*Hq*2]; kept_host, skipped_host: host uint64 [B*Hq].
@@ -243,7 +268,7 @@ int bsfa_skip_stats(const uint64_t* stats_dev, int32_t B, int32_t Hq, uint64_t* 
 /* Thread-local text for the last failing call on this thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* Library ABI version (this header: 3). */
+/* Library ABI version (this header: 4). */
 int32_t bsfa_abi_version(void);
 
 #ifdef __cplusplus

@@ -23,10 +23,11 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert set(names) >= {"bsfa_build_block_lists", "bsfa_fwd", "bsfa_skip_stats",
                           "bsfa_last_error", "bsfa_abi_version", "bsfa_decode",
-                          "bsfa_decode_workspace_size"}
+                          "bsfa_decode_workspace_size", "bsfa_calibrate_tau",
+                          "bsfa_calibrate_workspace_size"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.bsfa_abi_version() == 3
+    assert lib.bsfa_abi_version() == 4
 
 
 def test_two_call_sizing_and_too_small():
@@ -238,3 +239,41 @@ def test_block_list_cache_is_bounded(monkeypatch):
     # 64 was reused before 256 evicted the oldest (128), so 128 is built again
     assert calls == [64, 128, 192, 256, 128]
     assert list(k[1] for k in Fake._cache) == [64, 256, 128]
+
+
+def _calib_call(lib, **kw):
+    args = dict(tm=16, keep=16, B=2, Hq=4, n=100, q=0.5, tau=16, ws=16, ws_bytes=1 << 20)
+    args.update(kw)
+    return lib.bsfa_calibrate_tau(args["tm"], args["keep"], args["B"], args["Hq"], args["n"],
+                                  args["q"], args["tau"], args["ws"], args["ws_bytes"], None)
+
+
+def test_calibrate_workspace_size():
+    lib = bsfa.load_library()
+    nb = ctypes.c_int64(0)
+    assert lib.bsfa_calibrate_workspace_size(8, ctypes.byref(nb)) == 0
+    assert nb.value >= 8 * 256 * 4
+    assert lib.bsfa_calibrate_workspace_size(0, ctypes.byref(nb)) == -1
+    assert lib.bsfa_calibrate_workspace_size(8, None) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -1),
+    (dict(Hq=0), -1),
+    (dict(n=-5), -1),
+    (dict(q=-0.1), -1),
+    (dict(q=1.5), -1),
+    (dict(q=float("nan")), -1),
+    (dict(tau=None), -1),
+    (dict(ws=None), -1),
+    (dict(tm=None), -1),
+    (dict(keep=None), -1),
+    (dict(ws_bytes=100), -3),                 # workspace too small
+    (dict(ws=8), -2),                         # misaligned workspace
+    (dict(tm=18), -2),                        # misaligned maxima
+    (dict(B=1 << 16, n=1 << 16), -2),         # 2^32 blocks per head
+])
+def test_calibrate_argument_errors(kw, code):
+    lib = bsfa.load_library()
+    assert _calib_call(lib, **kw) == code
+    assert lib.bsfa_last_error() != b""
