@@ -80,3 +80,27 @@ def test_decode_bytes_closed_form():
     keep[:, :, 0] = True
     got = bench.decode_bytes(w, lengths, keep)
     assert got == expect - (rows - 64 * w.B) * w.Hkv * w.d * 2
+
+
+def test_more_than_one_gpu_is_refused():
+    """The library has no multi-GPU path: --gpus above 1 exits with a message, before
+    anything touches a GPU."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=bench.ROOT,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_leg_on_a_small_workload():
+    """The cpu_baseline leg times the oracle on stratified panels and counts executed FLOP
+    as the GPU line does (every allowed tile's QK^T, the kept tiles' P.V)."""
+    from block_sparse_flashattention_amd import inputs
+
+    w = inputs.WORKLOADS["single_head_1k"]
+    r = bench.cpu_baseline(w, None, budget_s=0.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] > 0.0 and r["cores"] >= 1 and r["elapsed_s"] > 0.0
+    assert r["sample"].startswith("2 (query tile, head) panels")
