@@ -117,7 +117,7 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes}))
 
 
-def cpu_baseline(w, taus_gpu_unused, budget_s: float = 20.0):
+def cpu_baseline(w, budget_s: float = 20.0):
     """Time the fp64 CPU oracle on a bounded, stratified sample of query tiles."""
     from block_sparse_flashattention_amd import inputs
     from oracle import bsfa_oracle as orc
@@ -167,13 +167,14 @@ def cpu_baseline(w, taus_gpu_unused, budget_s: float = 20.0):
     return {
         "value": flop / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": min(cores, blas_threads) if blas_threads > 1 else 1,
+        "cores": min(cores, blas_threads),
         "kind": "oracle",
         "sample": (f"{len(done)} (query tile, head) panels of the same workload, stratified "
                    f"over tiles {tiles} x heads {heads}, taus from the oracle's own "
                    f"calibration; executed FLOP counted like the GPU's; "
-                   f"{elapsed:.1f} s of fp64 numpy on {cores} visible cores, "
-                   f"BLAS threads {blas_threads}"),
+                   f"{elapsed:.1f} s of fp64 numpy; the matrix products run on "
+                   f"{min(cores, blas_threads)} BLAS threads ({cores} cores visible), "
+                   f"the rest of the oracle on one"),
         "elapsed_s": elapsed,
     }
 
@@ -301,6 +302,7 @@ def bench_decode(args, w):
     gated_bytes = decode_bytes(w, lengths, keep)
     dense_bytes = decode_bytes(w, lengths, None)
     value = gated_bytes / (gated_ms / 1e3) / 1e9
+    dtraffic = measured_decode_traffic(w.name, args.quantile)
     achieved = gated_bytes / (gated_kern / 1e3) / 1e9
     line = {
         "metric": "BSFA decode step, algorithmic HBM GB/s (one new token per sequence)",
@@ -320,7 +322,9 @@ def bench_decode(args, w):
                    "tau_quantile": args.quantile, "block": "1x64"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_decode_traffic(w.name, args.quantile)},
+                     "traffic": dtraffic},
+        "hbm_measured_gbs": (None if dtraffic is None
+                             else round(dtraffic / (gated_kern / 1e3) / 1e9, 1)),
         "tokens_per_s": round(w.B / (gated_ms / 1e3), 1),
         "dense_path_ms": round(dense_ms, 5),
         "dense_path_gbs": round(dense_bytes / (dense_kern / 1e3) / 1e9, 1),
@@ -346,8 +350,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sink_local_64k")
     ap.add_argument("--quantile", type=float, default=0.5)
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time every calibrated quantile of the workload and tau=-inf")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false",
+                    help="time only --quantile (by default every calibrated quantile of "
+                         "the workload and tau=-inf are timed too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true")
@@ -471,6 +476,7 @@ def main():
         gate_ms, _, _, _ = timed(torch.full((w.Hq,), -math.inf, device=dev), "gated tau=-inf")
 
     head = results[args.quantile]
+    traffic = measured_traffic(w.name, args.quantile)
     value = head["exec_flop"] / (head["ms"] / 1e3) / 1e12
     achieved = head["exec_flop"] / (head["kernel_ms"] / 1e3) / 1e12
     line = {
@@ -494,7 +500,7 @@ def main():
                    "out_dtype": "f32" if w.out_f32 else "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, args.quantile)},
+                     "traffic": traffic},
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(dense_flop / (head["ms"] / 1e3) / 1e12, 2),
         "dense_path_ms": round(dense_ms, 4),
@@ -504,6 +510,11 @@ def main():
         "skip_fraction_allowed": round(head["skip_allowed"], 4),
         "kernel_ms_mean": round(head["kernel_ms"], 4),
         "hbm_algorithmic_gbs": round(alg_bytes / (head["kernel_ms"] / 1e3) / 1e9, 1),
+        # HBM bytes the counters measured for one gated launch (null when the committed
+        # record does not match this kernel source, workload and quantile) per kernel time
+        "hbm_measured_gbs": (None if traffic is None
+                             else round(traffic / (head["kernel_ms"] / 1e3) / 1e9, 1)),
+        "hbm_peak_gbs": PEAK_HBM_GBS,
         "block_lists_host_ms": round(lists_host_s * 1e3, 2),
         "calibration_pass_ms": round(float(np.mean(cal_ms)), 4),
         "calibration_total_ms": round(calib_total_ms, 3),
@@ -521,7 +532,7 @@ def main():
         del q, k, v, out, lse
         torch.cuda.empty_cache()
         log("[bench] timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(w, taus, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

@@ -216,6 +216,29 @@ def _buffer(name, t, shape, dtypes, contiguous=True):
         raise BsfaError(-2, f"{name} must be contiguous")
 
 
+def _stream_scope(stream, dev):
+    """(context, handle) for a call that launches on ``stream``.
+
+    With no stream the call runs on torch's current stream. With a caller stream (a
+    hipStream_t handle) every temporary the call allocates (counters, a tau copy, the
+    decode or calibration workspace, outputs not passed in) is allocated and filled with
+    that stream current: its zero-fill or copy is queued before the kernel on the same
+    stream, and the caching allocator hands the memory out again only to that stream, so
+    it cannot be reused while the launch is pending. Inputs the caller passes in must be
+    ready on that stream (the caller orders them, as for any stream argument)."""
+    import contextlib
+
+    import torch
+
+    if stream is None:
+        return contextlib.nullcontext(), torch.cuda.current_stream(dev).cuda_stream
+    handle = int(stream)
+    default = torch.cuda.default_stream(dev)
+    ext = default if handle == default.cuda_stream else torch.cuda.ExternalStream(
+        handle, device=dev)
+    return torch.cuda.stream(ext), handle
+
+
 def _strides(t) -> _CStrides:
     s = t.stride()
     if s[3] != 1:
@@ -227,7 +250,8 @@ def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0
         out_dtype=None, out=None, want_lse: bool = True, stats: bool = False,
         export_tiles: bool = False, lists: BlockLists | None = None, stream=None,
         lse_out=None, stats_out=None) -> FwdResult:
-    """Block-sparse attention forward on the GPU (asynchronous on the current stream).
+    """Block-sparse attention forward on the GPU, asynchronous on ``stream`` (a
+    hipStream_t handle; default torch's current stream).
 
     q: bf16 [B, Hq, N, d]; k, v: bf16 [B, Hkv, N, d] (CUDA/HIP tensors, last dim
     contiguous). tau: None (dense path) or fp32 tensor [Hq] on the device (or anything
@@ -248,56 +272,56 @@ def fwd(q, k, v, mask: MaskSpec = MaskSpec(), tau=None, softmax_scale: float = 0
         raise BsfaError(-1, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     dev = q.device
     _on_device(dev, q=q, k=k, v=v, out=out, lse_out=lse_out, stats_out=stats_out)
-    if out_dtype is None:
-        out_dtype = torch.bfloat16
-    if out is None:
-        out = torch.empty((bsz, hq, n, d), dtype=out_dtype, device=dev)
-    _buffer("out", out, (bsz, hq, n, d), (torch.bfloat16, torch.float32), contiguous=False)
-    if lse_out is not None:
-        _buffer("lse_out", lse_out, (bsz, hq, n), (torch.float32,))
-        lse = lse_out
-    else:
-        lse = torch.empty((bsz, hq, n), dtype=torch.float32, device=dev) if want_lse else None
-    if stats_out is not None:
-        _buffer("stats_out", stats_out, (bsz, hq, 2), (torch.int64,))
-    if lists is None:
-        lists = BlockLists.get(mask, n, dev)
-    _on_device(dev, lists=lists.row_ptr)
-    tau_t = None
-    if tau is not None:
-        tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
-        if tau_t.numel() == 1 and hq > 1:
-            tau_t = tau_t.expand(hq).contiguous()
-        if tau_t.numel() != hq:
-            raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
-        tau_t = tau_t.contiguous()
-    if stats_out is not None:
-        st = stats_out
-    else:
-        st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
-    tm = kp = None
-    if export_tiles:
-        tm = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.float32, device=dev)
-        kp = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.uint8, device=dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    cm = mask._c()
-    cl = lists._c()
-    sq, sk, sv, so = _strides(q), _strides(k), _strides(v), _strides(out)
-    status = lib.bsfa_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-        lse.data_ptr() if lse is not None else None, bsz, hq, hkv, n, d,
-        ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
-        ctypes.byref(cm), ctypes.byref(cl),
-        tau_t.data_ptr() if tau_t is not None else None, float(softmax_scale),
-        OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
-        st.data_ptr() if st is not None else None,
-        tm.data_ptr() if tm is not None else None,
-        kp.data_ptr() if kp is not None else None, stream)
-    _check(lib, status)
-    if tm is not None and lists.nnz == 0:
-        tm, kp = tm[..., :0], kp[..., :0]
-    return FwdResult(out, lse, st, tm, kp, lists)
+    scope, stream = _stream_scope(stream, dev)
+    with scope:
+        if out_dtype is None:
+            out_dtype = torch.bfloat16
+        if out is None:
+            out = torch.empty((bsz, hq, n, d), dtype=out_dtype, device=dev)
+        _buffer("out", out, (bsz, hq, n, d), (torch.bfloat16, torch.float32), contiguous=False)
+        if lse_out is not None:
+            _buffer("lse_out", lse_out, (bsz, hq, n), (torch.float32,))
+            lse = lse_out
+        else:
+            lse = torch.empty((bsz, hq, n), dtype=torch.float32, device=dev) if want_lse else None
+        if stats_out is not None:
+            _buffer("stats_out", stats_out, (bsz, hq, 2), (torch.int64,))
+        if lists is None:
+            lists = BlockLists.get(mask, n, dev)
+        _on_device(dev, lists=lists.row_ptr)
+        tau_t = None
+        if tau is not None:
+            tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
+            if tau_t.numel() == 1 and hq > 1:
+                tau_t = tau_t.expand(hq).contiguous()
+            if tau_t.numel() != hq:
+                raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
+            tau_t = tau_t.contiguous()
+        if stats_out is not None:
+            st = stats_out
+        else:
+            st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
+        tm = kp = None
+        if export_tiles:
+            tm = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.float32, device=dev)
+            kp = torch.empty((bsz, hq, max(lists.nnz, 1)), dtype=torch.uint8, device=dev)
+        cm = mask._c()
+        cl = lists._c()
+        sq, sk, sv, so = _strides(q), _strides(k), _strides(v), _strides(out)
+        status = lib.bsfa_fwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, bsz, hq, hkv, n, d,
+            ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
+            ctypes.byref(cm), ctypes.byref(cl),
+            tau_t.data_ptr() if tau_t is not None else None, float(softmax_scale),
+            OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
+            st.data_ptr() if st is not None else None,
+            tm.data_ptr() if tm is not None else None,
+            kp.data_ptr() if kp is not None else None, stream)
+        _check(lib, status)
+        if tm is not None and lists.nnz == 0:
+            tm, kp = tm[..., :0], kp[..., :0]
+        return FwdResult(out, lse, st, tm, kp, lists)
 
 
 @dataclass
@@ -321,7 +345,8 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
            softmax_scale: float = 0.0, out_dtype=None, out=None, want_lse: bool = True,
            stats: bool = False, export_tiles: bool = False, workspace=None, stream=None,
            lse_out=None, stats_out=None) -> DecodeResult:
-    """One block-sparse decode step on the GPU (asynchronous on the current stream).
+    """One block-sparse decode step on the GPU, asynchronous on ``stream`` (a
+    hipStream_t handle; default torch's current stream).
 
     q: bf16 [B, Hq, d], the newest token's query per sequence and head; k_cache, v_cache:
     bf16 [B, Hkv, Lmax, d] (last dim contiguous); lengths: int32 [B] on the device, the
@@ -349,60 +374,60 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
     dev = q.device
     _on_device(dev, q=q, k_cache=k_cache, v_cache=v_cache, lengths=lengths, out=out,
                lse_out=lse_out, stats_out=stats_out, workspace=workspace)
-    if out_dtype is None:
-        out_dtype = torch.bfloat16
-    if out is None:
-        out = torch.empty((bsz, hq, d), dtype=out_dtype, device=dev)
-    _buffer("out", out, (bsz, hq, d), (torch.bfloat16, torch.float32), contiguous=False)
-    if out.stride(2) != 1:
-        raise BsfaError(-2, "the head dimension of out must be contiguous")
-    if lse_out is not None:
-        _buffer("lse_out", lse_out, (bsz, hq), (torch.float32,))
-        lse = lse_out
-    else:
-        lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if want_lse else None
-    if stats_out is not None:
-        _buffer("stats_out", stats_out, (bsz, hq, 2), (torch.int64,))
-    tau_t = None
-    if tau is not None:
-        tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
-        if tau_t.numel() == 1 and hq > 1:
-            tau_t = tau_t.expand(hq).contiguous()
-        if tau_t.numel() != hq:
-            raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
-        tau_t = tau_t.contiguous()
-    if stats_out is not None:
-        st = stats_out
-    else:
-        st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
-    nkb = -(-lmax // 64)
-    tm = kp = None
-    if export_tiles:
-        tm = torch.empty((bsz, hq, nkb), dtype=torch.float32, device=dev)
-        kp = torch.empty((bsz, hq, nkb), dtype=torch.uint8, device=dev)
-    need = decode_workspace_size(bsz, hq, lmax, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    elif not workspace.is_contiguous():
-        raise BsfaError(-2, "workspace must be contiguous")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    cm = mask._c()
-    sq = _CStrides(q.stride(0), q.stride(1), 0)
-    so = _CStrides(out.stride(0), out.stride(1), 0)
-    sk, sv = _strides(k_cache), _strides(v_cache)
-    status = lib.bsfa_decode(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(),
-        out.data_ptr(), lse.data_ptr() if lse is not None else None, bsz, hq, hkv, lmax, d,
-        ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
-        ctypes.byref(cm), tau_t.data_ptr() if tau_t is not None else None,
-        float(softmax_scale), OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
-        st.data_ptr() if st is not None else None,
-        tm.data_ptr() if tm is not None else None,
-        kp.data_ptr() if kp is not None else None,
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
-    _check(lib, status)
-    return DecodeResult(out, lse, st, tm, kp)
+    scope, stream = _stream_scope(stream, dev)
+    with scope:
+        if out_dtype is None:
+            out_dtype = torch.bfloat16
+        if out is None:
+            out = torch.empty((bsz, hq, d), dtype=out_dtype, device=dev)
+        _buffer("out", out, (bsz, hq, d), (torch.bfloat16, torch.float32), contiguous=False)
+        if out.stride(2) != 1:
+            raise BsfaError(-2, "the head dimension of out must be contiguous")
+        if lse_out is not None:
+            _buffer("lse_out", lse_out, (bsz, hq), (torch.float32,))
+            lse = lse_out
+        else:
+            lse = torch.empty((bsz, hq), dtype=torch.float32, device=dev) if want_lse else None
+        if stats_out is not None:
+            _buffer("stats_out", stats_out, (bsz, hq, 2), (torch.int64,))
+        tau_t = None
+        if tau is not None:
+            tau_t = torch.as_tensor(tau, dtype=torch.float32, device=dev).reshape(-1)
+            if tau_t.numel() == 1 and hq > 1:
+                tau_t = tau_t.expand(hq).contiguous()
+            if tau_t.numel() != hq:
+                raise BsfaError(-1, f"tau needs {hq} values, got {tau_t.numel()}")
+            tau_t = tau_t.contiguous()
+        if stats_out is not None:
+            st = stats_out
+        else:
+            st = torch.zeros((bsz, hq, 2), dtype=torch.int64, device=dev) if stats else None
+        nkb = -(-lmax // 64)
+        tm = kp = None
+        if export_tiles:
+            tm = torch.empty((bsz, hq, nkb), dtype=torch.float32, device=dev)
+            kp = torch.empty((bsz, hq, nkb), dtype=torch.uint8, device=dev)
+        need = decode_workspace_size(bsz, hq, lmax, d)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        elif not workspace.is_contiguous():
+            raise BsfaError(-2, "workspace must be contiguous")
+        cm = mask._c()
+        sq = _CStrides(q.stride(0), q.stride(1), 0)
+        so = _CStrides(out.stride(0), out.stride(1), 0)
+        sk, sv = _strides(k_cache), _strides(v_cache)
+        status = lib.bsfa_decode(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(),
+            out.data_ptr(), lse.data_ptr() if lse is not None else None, bsz, hq, hkv, lmax, d,
+            ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
+            ctypes.byref(cm), tau_t.data_ptr() if tau_t is not None else None,
+            float(softmax_scale), OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
+            st.data_ptr() if st is not None else None,
+            tm.data_ptr() if tm is not None else None,
+            kp.data_ptr() if kp is not None else None,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        _check(lib, status)
+        return DecodeResult(out, lse, st, tm, kp)
 
 
 def decode_calibration_maxima(q, k_cache, lengths, mask: MaskSpec, softmax_scale: float = 0.0,
@@ -413,10 +438,12 @@ def decode_calibration_maxima(q, k_cache, lengths, mask: MaskSpec, softmax_scale
     import torch
 
     hq = q.shape[1]
-    res = decode(q, k_cache, k_cache, lengths, mask=mask,
-                 tau=torch.full((hq,), math.nan, device=q.device),
-                 softmax_scale=softmax_scale, want_lse=False, export_tiles=True,
-                 stream=stream)
+    scope, stream = _stream_scope(stream, q.device)
+    with scope:
+        res = decode(q, k_cache, k_cache, lengths, mask=mask,
+                     tau=torch.full((hq,), math.nan, device=q.device),
+                     softmax_scale=softmax_scale, want_lse=False, export_tiles=True,
+                     stream=stream)
     torch.cuda.synchronize(q.device)
     tmax = res.tile_max.cpu().numpy()  # [B, Hq, nkb]
     keep = res.keep.cpu().numpy().astype(bool)  # forced blocks only (tau = NaN)
@@ -433,14 +460,14 @@ def decode_calibrate_tau(q, k_cache, lengths, mask: MaskSpec, quantile,
     import torch
 
     hq = q.shape[1]
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    res = decode(q, k_cache, k_cache, lengths, mask=mask,
-                 tau=torch.full((hq,), math.nan, device=q.device),
-                 softmax_scale=softmax_scale, want_lse=False, export_tiles=True,
-                 stream=stream)
-    nkb = -(-k_cache.shape[2] // 64)
-    return gpu_quantiles(res.tile_max, res.keep, q.shape[0], hq, nkb, quantile, stream)
+    scope, stream = _stream_scope(stream, q.device)
+    with scope:
+        res = decode(q, k_cache, k_cache, lengths, mask=mask,
+                     tau=torch.full((hq,), math.nan, device=q.device),
+                     softmax_scale=softmax_scale, want_lse=False, export_tiles=True,
+                     stream=stream)
+        nkb = -(-k_cache.shape[2] // 64)
+        return gpu_quantiles(res.tile_max, res.keep, q.shape[0], hq, nkb, quantile, stream)
 
 
 def calibrate_workspace_size(hq: int) -> int:
@@ -465,14 +492,14 @@ def gpu_quantiles(tile_max, keep, bsz: int, hq: int, n_blocks: int, quantile, st
         _buffer("tile_max", tile_max, (bsz, hq, n_blocks), (torch.float32,))
         _buffer("keep", keep, (bsz, hq, n_blocks), (torch.uint8,))
     qs = np.atleast_1d(np.asarray(quantile, dtype=np.float64))
-    taus = torch.empty((qs.size, hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(calibrate_workspace_size(hq), dtype=torch.uint8, device=dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    for i, qv in enumerate(qs):
-        _check(lib, lib.bsfa_calibrate_tau(tile_max.data_ptr(), keep.data_ptr(), bsz, hq,
-                                           n_blocks, float(qv), taus[i].data_ptr(),
-                                           ws.data_ptr(), ws.numel(), stream))
+    scope, stream = _stream_scope(stream, dev)
+    with scope:
+        taus = torch.empty((qs.size, hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(calibrate_workspace_size(hq), dtype=torch.uint8, device=dev)
+        for i, qv in enumerate(qs):
+            _check(lib, lib.bsfa_calibrate_tau(tile_max.data_ptr(), keep.data_ptr(), bsz, hq,
+                                               n_blocks, float(qv), taus[i].data_ptr(),
+                                               ws.data_ptr(), ws.numel(), stream))
     torch.cuda.synchronize(dev)  # the launches may sit on a stream other than torch's
     out = taus.cpu().numpy()
     return out[0] if np.ndim(quantile) == 0 else out
@@ -508,9 +535,11 @@ def calibration_maxima(q, k, mask: MaskSpec, softmax_scale: float = 0.0, lists=N
     import torch
 
     hq = q.shape[1]
-    res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), math.nan, device=q.device),
-              softmax_scale=softmax_scale, want_lse=False, export_tiles=True, lists=lists,
-              stream=stream)
+    scope, stream = _stream_scope(stream, q.device)
+    with scope:
+        res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), math.nan, device=q.device),
+                  softmax_scale=softmax_scale, want_lse=False, export_tiles=True, lists=lists,
+                  stream=stream)
     torch.cuda.synchronize(q.device)  # the launch may sit on a stream other than torch's
     tmax = res.tile_max.cpu().numpy()  # [B, Hq, nnz]
     eligible = (res.lists.cls_host & BSFA_CLS_FORCED) == 0
@@ -530,10 +559,10 @@ def calibrate_tau(q, k, mask: MaskSpec, quantile, softmax_scale: float = 0.0, li
     import torch
 
     hq = q.shape[1]
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), math.nan, device=q.device),
-              softmax_scale=softmax_scale, want_lse=False, export_tiles=True, lists=lists,
-              stream=stream)
-    return gpu_quantiles(res.tile_max, res.keep, q.shape[0], hq, res.lists.nnz, quantile,
-                         stream)
+    scope, stream = _stream_scope(stream, q.device)
+    with scope:
+        res = fwd(q, k, k, mask=mask, tau=torch.full((hq,), math.nan, device=q.device),
+                  softmax_scale=softmax_scale, want_lse=False, export_tiles=True, lists=lists,
+                  stream=stream)
+        return gpu_quantiles(res.tile_max, res.keep, q.shape[0], hq, res.lists.nnz,
+                             quantile, stream)

@@ -54,7 +54,7 @@ def reduced(w: inputs.Workload, qb, kb, vb, heads):
 
 
 def oracle_tau(w: inputs.Workload, quantile: float, q_tiles=None, heads=None,
-               seed: int = 1) -> np.ndarray:
+               seed: int = 1, scale=None) -> np.ndarray:
     """Per-head tau from the oracle's calibration on the calibration seed.
 
     With ``heads`` given, only those heads are calibrated (their KV groups generated);
@@ -64,7 +64,7 @@ def oracle_tau(w: inputs.Workload, quantile: float, q_tiles=None, heads=None,
     groups = sorted({h // w.group for h in heads})
     qb, kb, _ = inputs.generate(w, seed, groups=groups)
     q, k, _ = reduced(w, qb, kb, kb, heads)
-    taus = orc.calibrate_tau(q, k, oracle_spec(w), quantile, q_tiles=q_tiles)
+    taus = orc.calibrate_tau(q, k, oracle_spec(w), quantile, q_tiles=q_tiles, scale=scale)
     out = np.full(w.Hq, float(np.median(taus)))
     out[heads] = taus
     return out
@@ -93,8 +93,9 @@ class Report:
 
 
 def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
-            check_keep=True) -> Report:
-    """Compare one GPU result with the oracle on the selected query tiles and heads."""
+            check_keep=True, scale=None) -> Report:
+    """Compare one GPU result with the oracle on the selected query tiles and heads.
+    ``scale``: the softmax scale both sides use (None: 1/sqrt(d))."""
     spec = oracle_spec(w)
     nqt = -(-w.N // 64)
     q_tiles = list(range(nqt)) if q_tiles is None else list(q_tiles)
@@ -109,7 +110,7 @@ def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
         tmax_gpu = res.tile_max[:, heads].cpu().numpy().astype(np.float64)
         kd = dense_grid(res.lists, keep_gpu, q_tiles)
         md = dense_grid(res.lists, tmax_gpu, q_tiles)
-        ref = orc.attention(q, k, v, spec, tau=tau_r, q_tiles=q_tiles)
+        ref = orc.attention(q, k, v, spec, tau=tau_r, q_tiles=q_tiles, scale=scale)
         allowed = ref.allowed[None, None]
         tau_h = tau_r[None, :, None, None]
         near = (np.abs(ref.tile_max - tau_h) <= NEAR_TAU) & allowed & ~ref.forced[None, None]
@@ -125,7 +126,8 @@ def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
         override = kd
         kept = int((kd & allowed).sum())
         total = int(np.broadcast_to(allowed, kd.shape).sum())
-    ref = orc.attention(q, k, v, spec, tau=tau_r, q_tiles=q_tiles, keep_override=override)
+    ref = orc.attention(q, k, v, spec, tau=tau_r, q_tiles=q_tiles, keep_override=override,
+                        scale=scale)
     o_err, l_err = [], []
     for ti, t in enumerate(q_tiles):
         r0, r1 = t * 64, min(t * 64 + 64, w.N)
@@ -149,7 +151,8 @@ def compare(w: inputs.Workload, qb, kb, vb, res, tau, q_tiles=None, heads=None,
     return rep
 
 
-def run_gpu(w: inputs.Workload, qb, kb, vb, tau, export=True, stats=True, poison=True):
+def run_gpu(w: inputs.Workload, qb, kb, vb, tau, export=True, stats=True, poison=True,
+            scale=None):
     import torch
 
     import block_sparse_flashattention_amd as bsfa
@@ -160,7 +163,8 @@ def run_gpu(w: inputs.Workload, qb, kb, vb, tau, export=True, stats=True, poison
     out = torch.full((w.B, w.Hq, w.N, w.d), math.nan, dtype=out_dtype, device=dev) if poison else None
     tau_t = None if tau is None else torch.tensor(np.asarray(tau, dtype=np.float32), device=dev)
     res = bsfa.fwd(q, k, v, mask=gpu_spec(w), tau=tau_t, out_dtype=out_dtype, out=out,
-                   stats=stats, export_tiles=export and tau is not None)
+                   stats=stats, export_tiles=export and tau is not None,
+                   softmax_scale=0.0 if scale is None else float(scale))
     torch.cuda.synchronize()
     return res
 

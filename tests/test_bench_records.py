@@ -100,7 +100,7 @@ def test_cpu_baseline_leg_on_a_small_workload():
     from block_sparse_flashattention_amd import inputs
 
     w = inputs.WORKLOADS["single_head_1k"]
-    r = bench.cpu_baseline(w, None, budget_s=0.0)
+    r = bench.cpu_baseline(w, budget_s=0.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0.0 and r["cores"] >= 1 and r["elapsed_s"] > 0.0
     assert r["sample"].startswith("2 (query tile, head) panels")

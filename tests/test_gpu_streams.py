@@ -69,3 +69,54 @@ def test_two_streams_two_threads_match_sequential():
     # the two inputs differ, so equal results are not an accident of shared buffers
     assert not torch.equal(ref[0][0].out, ref[1][0].out)
     ph.log("two streams, two threads: bit-identical to sequential calls")
+
+
+def test_stream_argument_outside_a_stream_context():
+    """A call handed a stream other than torch's current one, outside any stream context,
+    while the current stream is still busy: the temporaries the call allocates (the
+    zeroed counters, the tau copy, the decode and calibration workspaces) are ordered on
+    the launch stream, so the results equal those of calls on the current stream."""
+    import torch
+
+    import block_sparse_flashattention_amd as bsfa
+
+    w = inputs.Workload("side_stream", 1, 8, 2, 1000, 128, causal=True, kind="planted",
+                        planted_frac=0.1)
+    dw = inputs.DecodeWorkload("side_stream_decode", 2, 8, 2, 900, 128, lengths=(900, 321),
+                               kind="sink_local")
+    ph.log(f"case stream argument without context: {w} and {dw}")
+    dev = torch.device("cuda")
+    mask = ph.gpu_spec(w)
+    tau = ph.oracle_tau(w, 0.5).astype(np.float32)
+    dtau = ph.oracle_tau_decode(dw, 0.5).astype(np.float32)
+    q, k, v = (ph.to_dev(x) for x in inputs.generate(w, 0))
+    qc, kc, _ = (ph.to_dev(x) for x in inputs.generate(w, 1))
+    dq, dk, dv, lengths = inputs.generate_decode(dw, 0)
+    dq, dk, dv = ph.to_dev(dq), ph.to_dev(dk), ph.to_dev(dv)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    ref = bsfa.fwd(q, k, v, mask=mask, tau=tau, stats=True, export_tiles=True)
+    dref = bsfa.decode(dq, dk, dv, lens, mask=mask, tau=dtau, stats=True)
+    tref = bsfa.calibrate_tau(qc, kc, mask, 0.5)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(20_000_000)  # keep the current stream busy for a while
+    got = bsfa.fwd(q, k, v, mask=mask, tau=tau, stats=True, export_tiles=True,
+                   stream=side.cuda_stream)
+    dgot = bsfa.decode(dq, dk, dv, lens, mask=mask, tau=dtau, stats=True,
+                       stream=side.cuda_stream)
+    tgot = bsfa.calibrate_tau(qc, kc, mask, 0.5, stream=side.cuda_stream)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(ref.out.view(torch.int16), got.out.view(torch.int16))
+    assert torch.equal(ref.lse, got.lse) and torch.equal(ref.stats, got.stats)
+    assert torch.equal(ref.keep, got.keep) and torch.equal(ref.tile_max, got.tile_max)
+    assert int(got.stats.sum()) == w.Hq * got.lists.nnz
+    assert torch.equal(dref.out.view(torch.int16), dgot.out.view(torch.int16))
+    assert torch.equal(dref.lse, dgot.lse) and torch.equal(dref.stats, dgot.stats)
+    assert np.array_equal(tref, tgot)
+    ph.log("stream argument without context: identical to calls on the current stream")
