@@ -20,13 +20,15 @@ Usage (bf16 CUDA tensors; q [B, Hq, N, d], k and v [B, Hkv, N, d], d = 64 or 128
 
 Calls are asynchronous on the current stream (or ``stream=``). With every output buffer
 passed in (``out=``, ``lse_out=``, ``stats_out=``, ``lists=``, ``workspace=``) they
-allocate nothing and can be captured in a HIP graph.
+allocate nothing and can be captured in a HIP graph. ``decode_static`` is the decode
+step for callers that cannot provide a workspace either: the library's fixed device
+scratch (32 MiB per GPU) holds the partials; calls that overlap on one GPU race.
 """
 _BINDING_NAMES = {
     "MaskSpec", "BlockLists", "BsfaError", "build_block_lists", "fwd", "skip_stats",
     "library_path", "load_library", "calibrate_tau", "calibration_maxima",
     "decode", "decode_workspace_size", "decode_calibrate_tau", "decode_calibration_maxima",
-    "gpu_quantiles", "calibrate_workspace_size",
+    "gpu_quantiles", "calibrate_workspace_size", "decode_static",
 }
 
 

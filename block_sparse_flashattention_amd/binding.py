@@ -51,7 +51,7 @@ class _CLists(ctypes.Structure):
 
 
 EXPORTED = ("bsfa_build_block_lists", "bsfa_fwd", "bsfa_skip_stats", "bsfa_last_error",
-            "bsfa_abi_version")
+            "bsfa_abi_version", "bsfa_decode", "bsfa_decode_static")
 
 
 def library_path() -> str:
@@ -89,6 +89,8 @@ def load_library():
         ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.bsfa_decode.restype = ctypes.c_int
+    lib.bsfa_decode_static.argtypes = lib.bsfa_decode.argtypes[:-3] + [ctypes.c_void_p]
+    lib.bsfa_decode_static.restype = ctypes.c_int
     lib.bsfa_calibrate_workspace_size.argtypes = [ctypes.c_int32, P(ctypes.c_int64)]
     lib.bsfa_calibrate_workspace_size.restype = ctypes.c_int
     lib.bsfa_calibrate_tau.argtypes = [
@@ -345,8 +347,8 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
            softmax_scale: float = 0.0, out_dtype=None, out=None, want_lse: bool = True,
            stats: bool = False, export_tiles: bool = False, workspace=None, stream=None,
            lse_out=None, stats_out=None) -> DecodeResult:
-    """One block-sparse decode step on the GPU, asynchronous on ``stream`` (a
-    hipStream_t handle; default torch's current stream).
+    """One block-sparse decode step on the GPU (bsfa_decode), asynchronous on ``stream``
+    (a hipStream_t handle; default torch's current stream).
 
     q: bf16 [B, Hq, d], the newest token's query per sequence and head; k_cache, v_cache:
     bf16 [B, Hkv, Lmax, d] (last dim contiguous); lengths: int32 [B] on the device, the
@@ -354,6 +356,28 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
     (dense path) or fp32 [Hq]. ``workspace`` is an optional caller buffer of at least
     decode_workspace_size bytes (a uint8 tensor); one is allocated here otherwise.
     """
+    return _decode(q, k_cache, v_cache, lengths, mask, tau, softmax_scale, out_dtype, out,
+                   want_lse, stats, export_tiles, workspace, stream, lse_out, stats_out,
+                   fixed_scratch=False)
+
+
+def decode_static(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
+                  softmax_scale: float = 0.0, out_dtype=None, out=None, want_lse: bool = True,
+                  stats: bool = False, export_tiles: bool = False, stream=None,
+                  lse_out=None, stats_out=None) -> DecodeResult:
+    """The decode step through bsfa_decode_static: the library's fixed device scratch
+    holds the per-split partials, so the library allocates nothing. Arguments as
+    ``decode`` without ``workspace``. Outputs that are not passed in (out, lse_out,
+    stats_out) and a tau that is not already an fp32 device tensor are still allocated
+    here by torch; a caller that may not allocate passes them all in."""
+    return _decode(q, k_cache, v_cache, lengths, mask, tau, softmax_scale, out_dtype, out,
+                   want_lse, stats, export_tiles, None, stream, lse_out, stats_out,
+                   fixed_scratch=True)
+
+
+def _decode(q, k_cache, v_cache, lengths, mask, tau, softmax_scale, out_dtype, out,
+            want_lse, stats, export_tiles, workspace, stream, lse_out, stats_out,
+            fixed_scratch: bool) -> DecodeResult:
     import torch
 
     lib = load_library()
@@ -407,16 +431,17 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
         if export_tiles:
             tm = torch.empty((bsz, hq, nkb), dtype=torch.float32, device=dev)
             kp = torch.empty((bsz, hq, nkb), dtype=torch.uint8, device=dev)
-        need = decode_workspace_size(bsz, hq, lmax, d)
-        if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-        elif not workspace.is_contiguous():
-            raise BsfaError(-2, "workspace must be contiguous")
+        if not fixed_scratch:
+            need = decode_workspace_size(bsz, hq, lmax, d)
+            if workspace is None:
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            elif not workspace.is_contiguous():
+                raise BsfaError(-2, "workspace must be contiguous")
         cm = mask._c()
         sq = _CStrides(q.stride(0), q.stride(1), 0)
         so = _CStrides(out.stride(0), out.stride(1), 0)
         sk, sv = _strides(k_cache), _strides(v_cache)
-        status = lib.bsfa_decode(
+        args = [
             q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(),
             out.data_ptr(), lse.data_ptr() if lse is not None else None, bsz, hq, hkv, lmax, d,
             ctypes.byref(sq), ctypes.byref(sk), ctypes.byref(sv), ctypes.byref(so),
@@ -424,8 +449,12 @@ def decode(q, k_cache, v_cache, lengths, mask: MaskSpec = MaskSpec(), tau=None,
             float(softmax_scale), OUT_F32 if out.dtype == torch.float32 else OUT_BF16,
             st.data_ptr() if st is not None else None,
             tm.data_ptr() if tm is not None else None,
-            kp.data_ptr() if kp is not None else None,
-            workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+            kp.data_ptr() if kp is not None else None]
+        if fixed_scratch:
+            status = lib.bsfa_decode_static(*args, stream)
+        else:
+            status = lib.bsfa_decode(*args, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), stream)
         _check(lib, status)
         return DecodeResult(out, lse, st, tm, kp)
 

@@ -31,10 +31,20 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/bsfa.h"
 #include "bsfa_internal.h"
 
 namespace bsfa {
+
+// Fixed device scratch for bsfa_decode_static, for callers that cannot allocate: the
+// per-split partials live here instead of in a caller workspace. Every GPU the library
+// runs on holds its own copy until the process ends. Host code never passes this name to
+// a kernel (on the host it is only a stand-in for the symbol); it uses the device address
+// that hipGetSymbolAddress returns for the device in question.
+static __device__ __align__(256) unsigned char scratch[DEC_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 #include "bsfa_device.h"
@@ -435,7 +445,46 @@ hipError_t launch_decode_d(const DecArgs& a, bool out_f32, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Device address of `scratch` on each device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+int decode_static_scratch(void* stream, void** ptr, const char** err) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = hipGetErrorString(e);
+    return BSFA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = "device index out of range for the fixed decode scratch";
+    return BSFA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // look the symbol up with the stream's device current, then restore the caller's
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || p == nullptr) {
+      *err = e != hipSuccess ? hipGetErrorString(e) : "no device address for the scratch";
+      return BSFA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BSFA_OK;
+}
 
 int launch_decode(const DecArgs& a, int d, bool out_f32, void* stream, const char** err) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

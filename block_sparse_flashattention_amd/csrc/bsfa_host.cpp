@@ -215,7 +215,7 @@ extern "C" {
 
 const char* bsfa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t bsfa_abi_version(void) { return 4; }
+int32_t bsfa_abi_version(void) { return 5; }
 
 int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_q,
                            int32_t block_k, int32_t* row_ptr, int32_t* col, uint8_t* cls,
@@ -382,13 +382,19 @@ int bsfa_decode_workspace_size(int32_t B, int32_t Hq, int32_t max_len, int32_t d
   return ok();
 }
 
-int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
+}  // extern "C"
+
+namespace {
+
+// bsfa_decode and bsfa_decode_static. With fixed_scratch the per-split partials go to the
+// library's fixed device scratch (workspace and workspace_bytes are ignored).
+int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
                 int32_t Hkv, int32_t max_len, int32_t d, const bsfa_strides* sq,
                 const bsfa_strides* sk, const bsfa_strides* sv, const bsfa_strides* so,
                 const bsfa_mask_spec* mask, const float* tau, float softmax_scale,
                 int32_t out_dtype, uint64_t* stats, float* tile_max, uint8_t* keep,
-                void* workspace, int64_t workspace_bytes, void* stream) {
+                void* workspace, int64_t workspace_bytes, bool fixed_scratch, void* stream) {
   if (B < 0 || Hq < 1 || Hkv < 1 || max_len < 1)
     return fail(BSFA_ERR_INVALID_ARG, "need B >= 0, Hq >= 1, Hkv >= 1, max_len >= 1");
   if (Hq % Hkv != 0) return fail(BSFA_ERR_INVALID_ARG, "Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
@@ -408,7 +414,7 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (Hq / Hkv > 32)
     return fail(BSFA_ERR_UNSUPPORTED, "more than 32 query heads per KV head (%d)", Hq / Hkv);
   if (B == 0) return ok();
-  if (!q || !k_cache || !v_cache || !lengths || !out || !workspace)
+  if (!q || !k_cache || !v_cache || !lengths || !out || (!workspace && !fixed_scratch))
     return fail(BSFA_ERR_INVALID_ARG,
                 "q, k_cache, v_cache, lengths, out and workspace are required");
   if (!sq || !sk || !sv || !so) return fail(BSFA_ERR_INVALID_ARG, "strides are required");
@@ -417,19 +423,30 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!view_fits(sk, max_len, d) || !view_fits(sv, max_len, d))
     return fail(BSFA_ERR_UNSUPPORTED, "the K or V rows of one head span 2^31 bytes or more");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      !aligned16(workspace))
+      (!fixed_scratch && !aligned16(workspace)))
     return fail(BSFA_ERR_UNSUPPORTED,
                 "q, k_cache, v_cache, out and workspace must be 16-byte aligned");
   if ((uintptr_t)lengths & 3u) return fail(BSFA_ERR_UNSUPPORTED, "lengths must be 4-byte aligned");
   const int32_t nsplit = decode_splits(max_len);
   const int64_t need = (int64_t)B * Hq * nsplit * (d + 4) * (int64_t)sizeof(float);
-  if (workspace_bytes < need)
+  if (fixed_scratch && need > bsfa::DEC_STATIC_SCRATCH_BYTES)
+    return fail(BSFA_ERR_BUFFER_TOO_SMALL,
+                "this decode step needs %lld bytes of scratch; the fixed scratch of "
+                "bsfa_decode_static holds %lld (use bsfa_decode with a workspace)",
+                (long long)need, (long long)bsfa::DEC_STATIC_SCRATCH_BYTES);
+  if (!fixed_scratch && workspace_bytes < need)
     return fail(BSFA_ERR_BUFFER_TOO_SMALL, "workspace %lld bytes < %lld",
                 (long long)workspace_bytes, (long long)need);
   // one dispatch counts its work-items in 32 bits
   if ((int64_t)B * Hkv * nsplit * bsfa::DEC_SPLIT_THREADS > (int64_t)UINT32_MAX ||
       (int64_t)B * Hq * (d / 32) * bsfa::DEC_COMBINE_THREADS > (int64_t)UINT32_MAX)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+
+  const char* err = nullptr;
+  if (fixed_scratch) {
+    const int rc = bsfa::decode_static_scratch(stream, &workspace, &err);
+    if (rc != BSFA_OK) return fail(rc, "%s", err ? err : "fixed scratch unavailable");
+  }
 
   bsfa::DecArgs a;
   memset(&a, 0, sizeof a);
@@ -469,10 +486,37 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.stats = (unsigned long long*)stats;
   a.tile_max = tile_max;
   a.keep = keep;
-  const char* err = nullptr;
   const int rc = bsfa::launch_decode(a, d, out_dtype == BSFA_OUT_F32, stream, &err);
   if (rc != BSFA_OK) return fail(rc, "%s", err ? err : "launch failed");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
+                int32_t Hkv, int32_t max_len, int32_t d, const bsfa_strides* sq,
+                const bsfa_strides* sk, const bsfa_strides* sv, const bsfa_strides* so,
+                const bsfa_mask_spec* mask, const float* tau, float softmax_scale,
+                int32_t out_dtype, uint64_t* stats, float* tile_max, uint8_t* keep,
+                void* workspace, int64_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, lengths, out, lse, B, Hq, Hkv, max_len, d, sq, sk,
+                     sv, so, mask, tau, softmax_scale, out_dtype, stats, tile_max, keep,
+                     workspace, workspace_bytes, false, stream);
+}
+
+int bsfa_decode_static(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t max_len, int32_t d, const bsfa_strides* sq,
+                       const bsfa_strides* sk, const bsfa_strides* sv,
+                       const bsfa_strides* so, const bsfa_mask_spec* mask, const float* tau,
+                       float softmax_scale, int32_t out_dtype, uint64_t* stats,
+                       float* tile_max, uint8_t* keep, void* stream) {
+  return decode_impl(q, k_cache, v_cache, lengths, out, lse, B, Hq, Hkv, max_len, d, sq, sk,
+                     sv, so, mask, tau, softmax_scale, out_dtype, stats, tile_max, keep,
+                     nullptr, 0, true, stream);
 }
 
 int bsfa_calibrate_workspace_size(int32_t Hq, int64_t* bytes) {

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/bsfa.h"
+
 namespace bsfa {
 
 // Everything one forward launch needs, passed by value as the kernel argument.
@@ -74,6 +76,13 @@ struct DecArgs {
 
 // Launches the decode split kernel and the combine kernel on `stream`.
 int launch_decode(const DecArgs& a, int d, bool out_f32, void* stream, const char** err);
+
+// Bytes of the fixed device scratch that bsfa_decode_static uses in place of a workspace.
+constexpr int64_t DEC_STATIC_SCRATCH_BYTES = BSFA_DECODE_STATIC_SCRATCH_BYTES;
+
+// Device address of the fixed decode scratch on the device of `stream` (looked up once per
+// device). 0 or a negative bsfa_status; *err receives a static message on failure.
+int decode_static_scratch(void* stream, void** ptr, const char** err);
 
 // Per-head threshold calibration from exported block maxima (bsfa_calib.hip).
 struct CalibState {

@@ -232,6 +232,34 @@ int bsfa_decode(const void* q, const void* k_cache, const void* v_cache,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * bsfa_decode_static: bsfa_decode without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc). The per-split partials that bsfa_decode keeps in the caller's
+ * workspace live instead in a fixed device array inside the library,
+ * BSFA_DECODE_STATIC_SCRATCH_BYTES (32 MiB) on every GPU the library runs on, held until
+ * the process ends. The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the array's device address is looked up once per device,
+ * on the first call for that device.
+ *   Arguments, layouts, ownership and results: as bsfa_decode, without workspace and
+ *   workspace_bytes. The launch goes to the device of `stream` (NULL: the current device).
+ * Errors: as bsfa_decode; a step that needs more scratch than the array holds
+ * (bsfa_decode_workspace_size above BSFA_DECODE_STATIC_SCRATCH_BYTES) returns
+ * BSFA_ERR_BUFFER_TOO_SMALL before any work is queued.
+ * Concurrency: every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs clearing: each call writes the partials it reads). Calls
+ * that overlap in time on one GPU (on different streams or host threads) race and give
+ * wrong results: the caller serialises them, e.g. on one stream.
+ */
+#define BSFA_DECODE_STATIC_SCRATCH_BYTES (32ll * 1024 * 1024)
+int bsfa_decode_static(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* lengths, void* out, float* lse, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t max_len, int32_t d, const bsfa_strides* sq,
+                       const bsfa_strides* sk, const bsfa_strides* sv,
+                       const bsfa_strides* so, const bsfa_mask_spec* mask, const float* tau,
+                       float softmax_scale, int32_t out_dtype, uint64_t* stats,
+                       float* tile_max, uint8_t* keep, void* stream);
+
+/*
  * Per-head threshold calibration on the GPU. Thresholds are learned once per layer and
  * head from the distribution of block maxima on calibration data (Block Sparse Flash
  * Attention, "The paper's improvements"); here tau_h is the `quantile` of head h's
@@ -268,7 +296,7 @@ int bsfa_skip_stats(const uint64_t* stats_dev, int32_t B, int32_t Hq, uint64_t* 
 /* Thread-local text for the last failing call on this thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* Library ABI version (this header: 4). */
+/* Library ABI version (this header: 5). */
 int32_t bsfa_abi_version(void);
 
 #ifdef __cplusplus

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
                           "bsfa_calibrate_workspace_size"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.bsfa_abi_version() == 4
+    assert lib.bsfa_abi_version() == 5
 
 
 def test_two_call_sizing_and_too_small():
@@ -277,3 +277,46 @@ def test_calibrate_argument_errors(kw, code):
     lib = bsfa.load_library()
     assert _calib_call(lib, **kw) == code
     assert lib.bsfa_last_error() != b""
+
+
+def _decode_static_call(lib, **kw):
+    args = dict(q=16, k=16, v=16, lengths=16, out=16, lse=None, B=2, Hq=8, Hkv=2, L=1024,
+                d=128, mask=binding._CMask(1, 0, 0, 1, 1), tau=None, scale=0.0, out_dtype=0,
+                stats=None, tile_max=None, keep=None)
+    args.update(kw)
+    sq = binding._CStrides(args["Hq"] * args["d"], args["d"], 0)
+    sk = binding._CStrides(args["Hkv"] * args["L"] * args["d"], args["L"] * args["d"],
+                           args["d"])
+    return lib.bsfa_decode_static(
+        args["q"], args["k"], args["v"], args["lengths"], args["out"], args["lse"], args["B"],
+        args["Hq"], args["Hkv"], args["L"], args["d"], ctypes.byref(sq), ctypes.byref(sk),
+        ctypes.byref(sk), ctypes.byref(sq),
+        ctypes.byref(args["mask"]) if args["mask"] is not None else None, args["tau"],
+        args["scale"], args["out_dtype"], args["stats"], args["tile_max"], args["keep"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=7), -1),
+    (dict(d=96), -2),
+    (dict(lengths=None), -1),
+    (dict(q=8), -2),                          # misaligned
+    (dict(tile_max=16, keep=16), -1),         # export without tau
+    # 2 * 64 * 512 splits * (128 + 4) * 4 bytes = 34.6 MB of partials > 32 MiB of scratch
+    (dict(B=2, Hq=64, Hkv=8, L=131072), -3),
+])
+def test_decode_static_argument_errors(kw, code):
+    """bsfa_decode_static validates like bsfa_decode, and rejects a step whose partials
+    exceed its fixed scratch, before any HIP call."""
+    lib = bsfa.load_library()
+    assert _decode_static_call(lib, **kw) == code
+    msg = lib.bsfa_last_error()
+    assert msg != b""
+    if code == -3:
+        assert b"fixed scratch" in msg and str(32 << 20).encode() in msg
+    # the largest step that fits: B * Hq * nsplit * (d + 4) * 4 <= 32 MiB
+    assert bsfa.decode_workspace_size(2, 64, 122880, 128) <= 32 << 20
+
+
+def test_decode_static_empty_batch_is_a_no_op():
+    lib = bsfa.load_library()
+    assert _decode_static_call(lib, B=0, q=None, out=None) == 0
