@@ -324,10 +324,13 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     return fail(BSFA_ERR_UNSUPPORTED, "q, k, v, out must be 16-byte aligned");
 
   const int group = Hq / Hkv;
+  // heads per workgroup; the workgroup's four members are hpack heads of 4 / hpack query
+  // tiles
   const int hpack = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-  const int64_t grid = (int64_t)B * (Hq / hpack) * nqt;
+  const int tq = 4 / hpack;
+  const int64_t grid = (int64_t)B * (Hq / hpack) * ((nqt + tq - 1) / tq);
   // one dispatch counts its work-items in 32 bits
-  const int64_t wg_threads = hpack == 4 ? 512 : 128 * hpack;
+  const int64_t wg_threads = 512;
   if (grid * wg_threads > (int64_t)UINT32_MAX)
     return fail(BSFA_ERR_UNSUPPORTED, "grid of %lld workgroups too large", (long long)grid);
 

@@ -110,7 +110,8 @@ int launch_calibrate(const CalibArgs& a, void* stream, const char** err);
 int64_t calibrate_grid(int64_t B, int64_t Hq, int64_t n_blocks);
 
 // Launches the forward kernel variant for head dim d, head pack hpack (query heads of
-// one KV group sharing a workgroup), gated (tau != null) or dense, bf16 or fp32 output.
+// one KV group sharing a workgroup: 4, 2 or 1, with 1, 2 or 4 query tiles each), gated
+// (tau != null) or dense, bf16 or fp32 output.
 // Returns 0 or a negative bsfa_status; *err receives a static message on failure.
 int launch_fwd(const FwdArgs& a, int d, int hpack, bool out_f32, void* stream,
                const char** err);

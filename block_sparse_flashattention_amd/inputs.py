@@ -78,6 +78,11 @@ WORKLOADS = {
     "sink_local_64k": Workload(
         "sink_local_64k", 1, 32, 8, 65536, 128, causal=True, kind="sink_local",
         tau_quantiles=(0.4, 0.5, 0.6)),
+    # multi-head attention (one query head per KV head) at the 64K sink/local shape: each
+    # workgroup serves four adjacent query tiles of one head
+    "mha_sink_local_64k": Workload(
+        "mha_sink_local_64k", 1, 32, 32, 65536, 128, causal=True, kind="sink_local",
+        tau_quantiles=(0.5,)),
     "gqa70b_planted_128k": Workload(
         "gqa70b_planted_128k", 1, 64, 8, 131072, 128, causal=True, n_global=128,
         kind="planted", planted_frac=0.05, tau_quantiles=(0.5,)),

@@ -42,6 +42,7 @@ def test_decode_traffic_record_only_for_its_workload():
     ("static_mask_4k", 7992, 0.01676),
     ("gqa_planted_16k", 1052672, 2.208),
     ("sink_local_64k", 16793600, 35.22),
+    ("mha_sink_local_64k", 16793600, 35.22),
     ("gqa70b_planted_128k", 134283264, 281.6),
 ])
 def test_flop_accounting_matches_tile_geometry(name, allowed_all_heads, dense_tflop):

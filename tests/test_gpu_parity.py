@@ -56,14 +56,19 @@ def test_static_mask_4k_dense_and_gated_minus_inf():
 
 
 @pytest.mark.parametrize("n,hq,hkv,d,causal,window,n_global,kind", [
-    (1000, 4, 2, 128, True, 0, 0, "planted"),       # ragged tail, 2 heads per workgroup
-    (200, 2, 2, 64, False, 90, 7, "gaussian"),      # ragged, non-causal window + globals
+    (1000, 4, 2, 128, True, 0, 0, "planted"),       # ragged tail, 2 heads x 2 query tiles
+    (200, 2, 2, 64, False, 90, 7, "gaussian"),      # ragged, non-causal window + globals, MHA
     (640, 8, 2, 128, True, 0, 0, "planted"),        # 4 heads per workgroup
     (520, 8, 2, 64, False, 150, 9, "gaussian"),     # 4 heads per workgroup at d = 64, ragged
     (300, 8, 1, 128, False, 0, 0, "gaussian"),      # two packs share one KV head, no mask
     (777, 3, 1, 64, True, 130, 64, "gaussian"),     # 3 query heads share one KV head
     (64, 1, 1, 128, True, 0, 0, "gaussian"),        # a single tile
     (1, 1, 1, 64, True, 0, 0, "gaussian"),          # a single token
+    # MHA: four query tiles per workgroup, 30 tiles (the last workgroup has two), windows
+    # so the four tiles' block lists differ
+    (1900, 4, 4, 128, True, 300, 64, "sink_local"),
+    # 2 heads x 2 query tiles, 23 tiles (the last workgroup has one), non-causal window
+    (1470, 6, 3, 64, False, 250, 20, "planted"),
 ])
 def test_small_shapes(n, hq, hkv, d, causal, window, n_global, kind):
     w = inputs.Workload(f"small_{kind}", 1, hq, hkv, n, d, causal=causal, window=window,
@@ -139,10 +144,11 @@ def test_gqa_planted_16k_sampled():
     ph.log(f"eligible skip fraction at the calibrated tau: {frac:.3f}")
 
 
-def _full_size(name, tiles_of, cal_of, dense_too=False):
+def _full_size(name, tiles_of, cal_of, dense_too=False, heads=None):
     w = W[name]
     nqt = w.N // 64
-    heads = [g * w.group + g % w.group for g in range(w.Hkv)]  # one query head per KV head
+    if heads is None:  # one query head per KV head
+        heads = [g * w.group + g % w.group for g in range(w.Hkv)]
     tiles = tiles_of(nqt)
     ph.log(f"case {name} (full size): B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d}; "
            f"oracle on heads {heads}, query tiles {tiles}")
@@ -171,3 +177,10 @@ def test_gqa70b_planted_128k_full_size_sampled():
     """The 70B-shaped layer (Hq=64, Hkv=8, N=131072, causal + 128 global tokens)."""
     _full_size("gqa70b_planted_128k", lambda n: [0, n // 2, n - 1],
                lambda n: [n // 3, (2 * n) // 3])
+
+
+def test_mha_sink_local_64k_full_size_sampled():
+    """Multi-head attention at the 64K sink/local shape (Hq = Hkv = 32): workgroups of four
+    adjacent query tiles of one head. Tiles 0 and 1 share a workgroup, as do the last two."""
+    _full_size("mha_sink_local_64k", lambda n: [0, 1, n // 2 + 1, n - 2, n - 1],
+               lambda n: [n // 4, n // 2, (3 * n) // 4], dense_too=True, heads=[0, 13, 31])
