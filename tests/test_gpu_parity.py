@@ -83,6 +83,19 @@ def test_batch_and_fp32_output():
     _case(w, tau_quantile=0.6)
 
 
+@pytest.mark.parametrize("b,hq,hkv,n,d", [
+    (2, 3, 3, 700, 64),    # one head x four query tiles; 11 tiles, the last workgroup has 3
+    (3, 4, 2, 450, 128),   # two heads x two query tiles; 8 tiles
+])
+def test_member_packs_batch_fp32_output(b, hq, hkv, n, d):
+    """Workgroups of query tiles (not only of heads) across a batch, with fp32 output and
+    a window, so the members' block lists differ in length and start."""
+    w = inputs.Workload(f"members_b{b}", b, hq, hkv, n, d, causal=True, window=200,
+                        n_global=10, kind="sink_local", out_f32=True)
+    _case(w, tau_quantile=0.5)
+    _case(w, tau=None)
+
+
 def test_batch_of_three_one_row_ragged_tail():
     """Three sequences of N = 129: the last query tile and key block hold one row each."""
     w = inputs.Workload("batch3_n129", 3, 8, 2, 129, 128, causal=True, kind="planted",
