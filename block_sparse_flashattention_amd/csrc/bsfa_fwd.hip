@@ -145,6 +145,7 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
   __shared__ uint32_t sFlag[2][HPACK];         // bit 0 keep, bits 1-2 rescale of rh 0/1
   __shared__ uint32_t sKeep[2];                // byte h: head h keeps the tile
   __shared__ float sL[HPACK][2][32];           // final row sums for the consumer
+  __shared__ int sCount;                       // the workgroup's step count (TQ > 1)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,7 +248,38 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
   cur_init(first);
   const int c_first = cur_col(first);  // kEnd: the workgroup has no steps
 
-  // Keep decisions of the pack for tile slot s (all heads), after a barrier.
+  // ---- the number of steps: the size of the union of the members' lists. With one
+  // query tile that is its list's length. With several, the workgroup marks the key
+  // blocks of its tiles' entries (one contiguous run of the lists) in an LDS bitmap,
+  // borrowed from the P buffers before their first use, and counts the marks.
+  int nsteps;
+  if constexpr (TQ == 1) {
+    nsteps = hi[0] - lo[0];
+  } else {
+    uint32_t* bits = reinterpret_cast<uint32_t*>(&sP[0][0][0][0][0]);
+    const int nwords = (nkb + 1 + 31) >> 5;  // key blocks 0 .. nkb (col_at's clamp)
+    int e_hi = hi[0];
+#pragma unroll
+    for (int m = 1; m < TQ; ++m) e_hi = max(e_hi, hi[m]);
+    for (int w = tid; w < nwords; w += 512) bits[w] = 0u;
+    if (tid == 0) sCount = 0;
+    __syncthreads();
+    for (int e = lo[0] + tid; e < e_hi; e += 512) {
+      int cb = a.col[e];
+      cb = cb < 0 ? 0 : (cb > nkb ? nkb : cb);
+      atomicOr(&bits[cb >> 5], 1u << (cb & 31));
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int w = tid; w < nwords; w += 512) cnt += __builtin_popcount(bits[w]);
+    if (cnt) atomicAdd(&sCount, cnt);
+    __syncthreads();
+    nsteps = __builtin_amdgcn_readfirstlane(sCount);
+    __syncthreads();  // the P buffers are free again
+  }
+
+  // Whether some member keeps the step in keep slot s (read by the consumers after the
+  // step's barrier): the V tile is staged only then.
   auto any_of = [&](int s) -> bool {
     if constexpr (GATE) return sKeep[s] != 0u;
     return true;
@@ -304,7 +336,6 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
       float mx[2];
       float tmax;
       bool keep;
-      bool any;
       bool in;  // the member's own list has this step's block
       int e;    // the member's entry of this step's block (when in)
     };
@@ -360,11 +391,9 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
     };
 
     f32x16_t sA[2][2], sB[2][2];
-    PState stA{{-INFINITY, -INFINITY}, 0.0f, false, false, false, 0};
-    PState stB{{-INFINITY, -INFINITY}, 0.0f, false, false, false, 0};
+    PState stA{{-INFINITY, -INFINITY}, 0.0f, false, false, 0};
+    PState stB{{-INFINITY, -INFINITY}, 0.0f, false, false, 0};
     Cursor nx = first;  // the next block to score
-    Cursor nx2 = first;  // one block further: the loop's bound when TQ > 1
-    if constexpr (TQ > 1) cur_next(nx2);
     // The member's part in the step at the cursor; moves the cursor on.
     auto take = [&](PState& st) -> int2 {
       const int c = cur_col(nx);
@@ -381,7 +410,6 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
       st.e = my_e;
       const int cls = st.in ? ldc_byte(a.cls, st.e) : 0;
       cur_next(nx);
-      if constexpr (TQ > 1) cur_next(nx2);
       return make_int2(c, cls);
     };
 
@@ -438,7 +466,6 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
       mask_max(sn, cn.x, cn.y, nxt.mx);
       gate(nxt, cn.y, (i + 1) & 1);
       __syncthreads();  // P(i), V(i), K(i+2) and the keep bytes of step i+1 are visible
-      nxt.any = any_of((i + 1) & 1);
       count_export(cur);
     };
 
@@ -459,24 +486,19 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
       mask_max(sA, c0.x, c0.y, stA.mx);
       gate(stA, c0.y, 0);
       __syncthreads();  // (2) keep bytes of step 0; every wave is done reading sK[0]
-      stA.any = any_of(0);
 
       // Unrolled by two so the scores alternate between sA and sB without copies. The
-      // loop has no exit between its two steps, and its bound is a count (one list) or a
-      // second cursor: other forms of the same control flow cost this compiler registers
-      // it does not have.
-      auto two_more = [&](int i) {  // steps i + 1 and i + 2 exist
-        if constexpr (TQ == 1) return i + 2 < hi[0] - lo[0];
-        else return cur_col(nx2) != kEnd;
-      };
+      // loop has no exit between its two steps, and its bound is the step count: other
+      // forms of the same control flow (an exit between the steps, a bound read from the
+      // cursors) cost this compiler registers it does not have.
       int i = 0;
-      for (; two_more(i); i += 2) {
+      for (; i + 2 < nsteps; i += 2) {  // steps i + 1 and i + 2 exist
         if (stA.keep) pstep(std::true_type{}, i, sA, stA, sB, stB);
         else pstep(std::false_type{}, i, sA, stA, sB, stB);
         if (stB.keep) pstep(std::true_type{}, i + 1, sB, stB, sA, stA);
         else pstep(std::false_type{}, i + 1, sB, stB, sA, stA);
       }
-      if (cur_col(nx) != kEnd) {
+      if (i + 1 < nsteps) {
         if (stA.keep) pstep(std::true_type{}, i, sA, stA, sB, stB);
         else pstep(std::false_type{}, i, sA, stA, sB, stB);
 #pragma unroll

@@ -333,6 +333,10 @@ int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   const int64_t wg_threads = 512;
   if (grid * wg_threads > (int64_t)UINT32_MAX)
     return fail(BSFA_ERR_UNSUPPORTED, "grid of %lld workgroups too large", (long long)grid);
+  // workgroups of several query tiles count their steps in a bitmap of nqt + 1 bits
+  if (tq > 1 && (int64_t)nqt + 1 > 524288)
+    return fail(BSFA_ERR_UNSUPPORTED,
+                "%d query tiles: more than 524287 with %d query heads per KV head", nqt, group);
 
   bsfa::FwdArgs a;
   memset(&a, 0, sizeof a);

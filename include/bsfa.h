@@ -157,7 +157,12 @@ int bsfa_build_block_lists(const bsfa_mask_spec* mask, int32_t N, int32_t block_
  * Pointers q, k, v, out must be 16-byte aligned and the n/h/b strides non-negative
  * multiples of 8. The K (and V) rows of one (batch, KV head), ((N - 1) * n-stride + d)
  * elements, must span fewer than 2^31 bytes; otherwise BSFA_ERR_UNSUPPORTED. So is a
- * launch of 2^32 or more work-items: B * Hq * ceil(N / 64) * 128 must stay below 2^32.
+ * launch of 2^32 or more work-items. A workgroup of 512 work-items serves four (query
+ * head, 64-row query tile) pairs of one KV head: P heads of 4 / P adjacent query tiles,
+ * P = 4, 2 or 1 as Hq / Hkv is a multiple of 4, even, or odd. So
+ * B * (Hq / P) * ceil(ceil(N / 64) / (4 / P)) * 512 must stay below 2^32, and for P < 4
+ * (the workgroup counts the union of its tiles' block lists in a 64 KiB LDS bitmap)
+ * ceil(N / 64) must stay below 524288.
  */
 int bsfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,

@@ -97,6 +97,10 @@ def _fwd_call(lib, **kw):
     (dict(sqn=-128), -2),                     # negative stride
     (dict(skn=1 << 24), -2),                  # one head's K/V rows span more than 2^31 bytes
     (dict(B=1 << 23), -2),                    # more than 2^32 work-items in one dispatch
+    # one query head per KV head: workgroups of four query tiles count their steps in a
+    # bitmap of ceil(N / 64) + 1 bits, at most 524288
+    (dict(Hq=2, Hkv=2, N=1 << 25, skn=0,
+          lists=binding._CLists(1 << 19, 64, 64, 3, 16, 16, 16)), -2),
 ])
 def test_fwd_argument_errors(kw, code):
     lib = bsfa.load_library()
