@@ -11,6 +11,9 @@ lists are built once per (mask, N) and cached, as in deployment; their host buil
 is reported separately. Inputs are resident in HBM before the timed region starts.
 
 Prints ONE JSON line (metric, value in executed TFLOP/s, roofline, cpu_baseline, ...).
+On the default workload the line also carries, under "decode", the decode step's own
+measurement (decode_sink_local_64k: algorithmic GB/s and its HBM roofline), taken after
+the prefill timing with the prefill tensors freed; --no-decode leaves it out.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
        python bench.py --workload decode_sink_local_64k   (the decode step instead)
@@ -234,8 +237,9 @@ def cpu_baseline_decode(w, lengths, budget_s: float = 20.0):
     }
 
 
-def bench_decode(args, w):
-    """Decode step: one new query row per sequence and head against the cache."""
+def bench_decode(args, w, with_cpu=True):
+    """Decode step: one new query row per sequence and head against the cache. Returns the
+    JSON record (with the CPU oracle's rate when with_cpu)."""
     import torch
 
     import block_sparse_flashattention_amd as bsfa
@@ -335,12 +339,12 @@ def bench_decode(args, w):
         "algorithmic_bytes_per_step": gated_bytes,
         "dense_bytes_per_step": dense_bytes,
     }
-    if not args.no_cpu_baseline:
-        del q, k, v
-        torch.cuda.empty_cache()
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    if with_cpu:
         log("[bench] timing the CPU oracle's decode")
         line["cpu_baseline"] = cpu_baseline_decode(w, lengths, args.cpu_budget)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def main():
@@ -354,6 +358,8 @@ def main():
                     help="time only --quantile (by default every calibrated quantile of "
                          "the workload and tau=-inf are timed too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", dest="decode", action="store_false",
+                    help="leave the decode step's measurement out of the default line")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -373,7 +379,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload in inputs.DECODE_WORKLOADS:
-        bench_decode(args, inputs.DECODE_WORKLOADS[args.workload])
+        line = bench_decode(args, inputs.DECODE_WORKLOADS[args.workload],
+                            with_cpu=not args.no_cpu_baseline)
+        print(json.dumps(line), flush=True)
         return
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
@@ -528,9 +536,17 @@ def main():
                                    "skip_fraction_eligible": round(r["skip_eligible"], 4)}
                          for qv, r in results.items()}
         line["gated_tau_minus_inf_ms"] = round(gate_ms, 4)
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    if args.decode and w.name == "sink_local_64k":
+        log("[bench] the decode step (decode_sink_local_64k)")
+        dl = bench_decode(args, inputs.DECODE_WORKLOADS["decode_sink_local_64k"], with_cpu=False)
+        line["decode"] = {"workload": dl["config"]["workload"]} | {
+            k_: dl[k_] for k_ in ("metric", "value", "unit", "ms_per_step", "kernel_ms_mean",
+                                  "roofline", "hbm_measured_gbs", "tokens_per_s",
+                                  "dense_path_ms", "speedup_vs_dense", "skip_fraction_allowed",
+                                  "v_blocks_skipped_fraction")}
     if not args.no_cpu_baseline:
-        del q, k, v, out, lse
-        torch.cuda.empty_cache()
         log("[bench] timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)
