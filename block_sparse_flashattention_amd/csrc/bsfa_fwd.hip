@@ -140,10 +140,10 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BLK * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BLK * VROW];
-  __shared__ bf16x8_t sP[2][HPACK][2][4][64];  // P^T operands: [buf][head][rh][ks][lane]
+  __shared__ bf16x8_t sP[2][HPACK][2][4][64];  // P^T operands: [buf][member][rh][ks][lane]
   __shared__ float sAlpha[2][HPACK][2][32];    // O rescale factor per row
   __shared__ uint32_t sFlag[2][HPACK];         // bit 0 keep, bits 1-2 rescale of rh 0/1
-  __shared__ uint32_t sKeep[2];                // byte h: head h keeps the tile
+  __shared__ uint32_t sKeep[2];                // byte h: member h keeps the tile
   __shared__ float sL[HPACK][2][32];           // final row sums for the consumer
   __shared__ int sCount;                       // the workgroup's step count (TQ > 1)
 
@@ -353,12 +353,18 @@ __global__ __launch_bounds__(512) void bsfa_fwd_ws_kernel(const FwdArgs a) {
         st.keep = st.in;
       }
     };
+    // Running reference max of each row (raw units), raised lazily: only when some row of
+    // the 32-row half grows past it by more than 2 in exp2 units (or gets its first keys),
+    // so P <= 4 and O rarely needs rescaling (2.7 % of row-half steps at the 64K sink/local
+    // shape). A larger margin rescales less, but then a row's dominant P is an arbitrary
+    // bf16-rounded value up to 2^margin instead of about 1: with 8 (P <= 256), rows whose
+    // weight sits on a few keys erred by up to 1.1e-2 in O.
     auto softmax_prep = [&](int rh, float mx, bool& rescale, float& alpha) -> float {
       float x0, x1;
       pair32(mx, x0, x1);
       const float m_new = fmaxf(m_run[rh], fmaxf(x0, x1));
       const bool grow =
-          (m_run[rh] == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run[rh]) * c2 > 8.0f);
+          (m_run[rh] == -INFINITY) ? (m_new != -INFINITY) : ((m_new - m_run[rh]) * c2 > 2.0f);
       rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
       alpha = 1.0f;
       if (rescale) {
