@@ -312,6 +312,50 @@ def test_brute_force_tiny(n, bq, bk, causal, window, n_global, tau):
     np.testing.assert_allclose(r.full_lse()[0, 0, :n], ref_l, atol=1e-12)
 
 
+def _staircase_inputs():
+    """Four 64-token blocks whose keys put every block maximum at a known integer.
+
+    d = 2 and scale 1, query rows of head h are (h + 1, 0), and key j is (x_j, 0) with
+    x_j = c + 1 at one key of block c and below c + 0.5 elsewhere. Any query row that
+    may attend a whole block c therefore has the block maximum (h + 1) * (c + 1) there:
+    on every eligible tile, since the off-diagonal tiles of a causal mask are full."""
+    n, nb = 256, 4
+    rng = np.random.default_rng(11)
+    x = np.empty(n)
+    for c in range(nb):
+        blk = rng.uniform(-1.0, c + 0.5, 64)
+        blk[int(rng.integers(0, 64))] = c + 1.0
+        x[c * 64:(c + 1) * 64] = blk
+    k = np.zeros((1, 1, n, 2))
+    k[0, 0, :, 0] = x
+    q = np.zeros((1, 2, n, 2))
+    q[0, 0, :, 0] = 1.0
+    q[0, 1, :, 0] = 2.0
+    return q, k
+
+
+@pytest.mark.parametrize("causal,diag,quantile,expected", [
+    # causal, diagonal forced: eligible (t, c < t) maxima c + 1 = {1, 1, 2, 1, 2, 3}
+    (True, True, 0.5, 1.5),   # sorted [1 1 1 2 2 3], position 2.5
+    (True, True, 0.4, 1.0),   # position 2.0
+    (True, True, 0.9, 2.5),   # position 4.5
+    # full mask, diagonal forced: every c three times, [1 1 1 2 2 2 3 3 3 4 4 4]
+    (False, True, 0.5, 2.5),  # position 5.5
+    (False, True, 0.2, 1.2),  # position 2.2
+    # full mask, nothing forced: every c four times
+    (False, False, 0.25, 1.75),  # position 3.75
+    (False, False, 1.0, 4.0),
+])
+def test_calibration_closed_form(causal, diag, quantile, expected):
+    """tau_h is the linear-interpolation quantile ("Block Sparse Flash Attention",
+    threshold calibration) of head h's eligible block maxima, here known exactly. Head 1's
+    scores are twice head 0's, so its tau is twice as large: the heads are not pooled."""
+    q, k = _staircase_inputs()
+    spec = MaskSpec(causal=causal, force_keep_diag=diag)
+    tau = orc.calibrate_tau(q, k, spec, quantile, scale=1.0)
+    np.testing.assert_allclose(tau, [expected, 2.0 * expected], rtol=0, atol=1e-12)
+
+
 def test_calibration_hits_target_fraction():
     n, d = 512, 16
     q, k = _rand((1, 2, n, d), 30), _rand((1, 1, n, d), 31)
