@@ -178,6 +178,28 @@ def test_calibration_hits_target_and_monotone_keep():
     assert np.all(lo.keep >= r.keep)
 
 
+@pytest.mark.parametrize("quantile,expected", [(0.5, 2.0), (0.25, 1.0), (0.9, 2.6), (0.0, 1.0)])
+def test_calibration_closed_form(quantile, expected):
+    """Closed form of the decode threshold: with key block c's largest score c + 1 for
+    head 0 (twice that for head 1), the rows at positions 255 and 191 have eligible
+    blocks {0, 1, 2} and {0, 1} (their own block is forced), so head 0's pooled maxima
+    are [1, 1, 2, 2, 3] and tau is their linear-interpolation quantile."""
+    lmax = 256
+    rng = np.random.default_rng(5)
+    x = np.empty(lmax)
+    for c in range(4):
+        blk = rng.uniform(-1.0, c + 0.5, 64)
+        blk[int(rng.integers(0, 64))] = c + 1.0
+        x[c * 64:(c + 1) * 64] = blk
+    k = np.zeros((2, 1, lmax, 2))
+    k[:, 0, :, 0] = x
+    q = np.zeros((2, 2, 2))
+    q[:, 0, 0] = 1.0
+    q[:, 1, 0] = 2.0
+    taus = orc.calibrate_tau_decode(q, k, [256, 192], MaskSpec(causal=True), quantile, scale=1.0)
+    np.testing.assert_allclose(taus, [expected, 2.0 * expected], rtol=0, atol=1e-12)
+
+
 def test_gate_ignores_statically_masked_keys():
     """Closed form: in the block that the window cuts, the keys outside the window score
     high and the keys inside score low, with tau between them. The block's maximum is
