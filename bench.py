@@ -286,12 +286,13 @@ def bench_decode(args, w, with_cpu=True):
             e_.record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t_start) / args.steps * 1e3
-        kern = float(np.mean([s_.elapsed_time(e_) for s_, e_ in evs]))
-        log(f"[bench] {label}: {wall:.4f} ms/step, kernels {kern:.4f} ms")
-        return wall, kern
+        ks = [s_.elapsed_time(e_) for s_, e_ in evs]
+        kern = float(np.mean(ks))
+        log(f"[bench] {label}: {wall:.4f} ms/step, kernels {kern:.4f} ms (min {np.min(ks):.4f})")
+        return wall, kern, float(np.median(ks)), float(np.min(ks))
 
-    dense_ms, dense_kern = timed(None, "dense decode (tau=NULL)")
-    gated_ms, gated_kern = timed(tau_t, f"gated decode tau@q={args.quantile}")
+    dense_ms, dense_kern, _, _ = timed(None, "dense decode (tau=NULL)")
+    gated_ms, gated_kern, gated_med, gated_min = timed(tau_t, f"gated decode tau@q={args.quantile}")
     res = bsfa.decode(q, k, v, lens, mask=mask, tau=tau_t, out=out, lse_out=lse, workspace=ws,
                       stats=True, export_tiles=True)
     torch.cuda.synchronize()
@@ -336,6 +337,8 @@ def bench_decode(args, w, with_cpu=True):
         "skip_fraction_allowed": round(skipped / max(kept + skipped, 1), 4),
         "v_blocks_skipped_fraction": round(1 - any_keep.sum() / max(allowed_g.sum(), 1), 4),
         "kernel_ms_mean": round(gated_kern, 5),
+        "kernel_ms_median": round(gated_med, 5),
+        "kernel_ms_min": round(gated_min, 5),
         "algorithmic_bytes_per_step": gated_bytes,
         "dense_bytes_per_step": dense_bytes,
     }
@@ -458,7 +461,8 @@ def main():
         st = stats.cpu().numpy()
         log(f"[bench] {label}: {wall / args.steps * 1e3:.3f} ms/step, kernel mean "
             f"{np.mean(kern_ms):.3f} ms (min {np.min(kern_ms):.3f})")
-        return wall / args.steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms)), st
+        return (wall / args.steps * 1e3, float(np.mean(kern_ms)), float(np.median(kern_ms)),
+                float(np.min(kern_ms)), st)
 
     qk_f, pv_f = tile_flops(w.d)
     allowed_tiles = lists.nnz * w.B * w.Hq
@@ -467,21 +471,22 @@ def main():
     alg_bytes = (2 * w.B * w.Hq * w.N * w.d * 2 + 2 * w.B * w.Hkv * w.N * w.d * 2
                  + w.B * w.Hq * w.N * 4) + (2 * w.B * w.Hq * w.N * w.d if w.out_f32 else 0)
 
-    dense_ms, dense_kern, _, _ = timed(None, "dense path (tau=NULL)")
+    dense_ms, dense_kern, dense_med, dense_min, _ = timed(None, "dense path (tau=NULL)")
 
     results = {}
     for qi, qv in enumerate(quantiles):
         tau_t = torch.tensor(taus[qi], dtype=torch.float32, device=dev)
-        ms, kern, kern_med, st = timed(tau_t, f"gated tau@q={qv}")
+        ms, kern, kern_med, kern_min, st = timed(tau_t, f"gated tau@q={qv}")
         kept, skipped = int(st[..., 0].sum()), int(st[..., 1].sum())
         exec_flop = kept * (qk_f + pv_f) + skipped * qk_f
-        results[qv] = dict(ms=ms, kernel_ms=kern, kernel_ms_median=kern_med, kept=kept,
+        results[qv] = dict(ms=ms, kernel_ms=kern, kernel_ms_median=kern_med,
+                           kernel_ms_min=kern_min, kept=kept,
                            skipped=skipped, exec_flop=exec_flop,
                            skip_eligible=skipped / max(allowed_tiles - forced_tiles, 1),
                            skip_allowed=skipped / max(allowed_tiles, 1))
     gate_ms = None
     if args.sweep:
-        gate_ms, _, _, _ = timed(torch.full((w.Hq,), -math.inf, device=dev), "gated tau=-inf")
+        gate_ms = timed(torch.full((w.Hq,), -math.inf, device=dev), "gated tau=-inf")[0]
 
     head = results[args.quantile]
     traffic = measured_traffic(w.name, args.quantile)
@@ -517,6 +522,10 @@ def main():
         "skip_fraction_eligible": round(head["skip_eligible"], 4),
         "skip_fraction_allowed": round(head["skip_allowed"], 4),
         "kernel_ms_mean": round(head["kernel_ms"], 4),
+        "kernel_ms_median": round(head["kernel_ms_median"], 4),
+        "kernel_ms_min": round(head["kernel_ms_min"], 4),
+        "dense_kernel_ms_median": round(dense_med, 4),
+        "dense_kernel_ms_min": round(dense_min, 4),
         "hbm_algorithmic_gbs": round(alg_bytes / (head["kernel_ms"] / 1e3) / 1e9, 1),
         # HBM bytes the counters measured for one gated launch (null when the committed
         # record does not match this kernel source, workload and quantile) per kernel time
