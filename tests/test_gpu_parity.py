@@ -157,9 +157,9 @@ def test_gqa_planted_16k_sampled():
     ph.log(f"eligible skip fraction at the calibrated tau: {frac:.3f}")
 
 
-def _full_size(name, tiles_of, cal_of, dense_too=False, heads=None):
-    w = W[name]
-    nqt = w.N // 64
+def _full_size(name, tiles_of, cal_of, dense_too=False, heads=None, w=None):
+    w = W[name] if w is None else w
+    nqt = (w.N + 63) // 64
     if heads is None:  # one query head per KV head
         heads = [g * w.group + g % w.group for g in range(w.Hkv)]
     tiles = tiles_of(nqt)
@@ -197,3 +197,14 @@ def test_mha_sink_local_64k_full_size_sampled():
     adjacent query tiles of one head. Tiles 0 and 1 share a workgroup, as do the last two."""
     _full_size("mha_sink_local_64k", lambda n: [0, 1, n // 2 + 1, n - 2, n - 1],
                lambda n: [n // 4, n // 2, (3 * n) // 4], dense_too=True, heads=[0, 13, 31])
+
+
+@pytest.mark.parametrize("name,heads", [("sink_local_64k", None),
+                                        ("mha_sink_local_64k", [0, 13, 31])])
+def test_ragged_64k_full_size_sampled(name, heads):
+    """The 64K sink/local shapes with N = 65536 - 37: the last query tile has 27 rows and
+    the last key block 27 keys, in both head groupings (four heads of a tile; four tiles of
+    a head, where the last workgroup's last member has the ragged tile)."""
+    w = inputs.scaled(W[name], N=65536 - 37)
+    _full_size(name, lambda n: [0, n // 2, n - 3, n - 2, n - 1],
+               lambda n: [n // 4, n // 2, (3 * n) // 4], heads=heads, w=w)
